@@ -1,0 +1,266 @@
+"""Paged-KV attention for AMD MI355X: thin Python binding of libpkv.so.
+
+The functions keep the names and argument order of FlashInfer's API pages
+(flashinfer.page.append_paged_kv_cache with get_seq_lens /
+get_batch_indices_positions from its Example;
+flashinfer.prefill.cudnn_batch_prefill_with_kv_cache;
+flashinfer.decode.trtllm_batch_decode_with_kv_cache). They only marshal
+arguments -- shapes, strides, dtypes, the current HIP stream -- and call the C
+ABI declared in include/pkv.h; every step of the computation runs in the HIP
+kernels. torch supplies device memory and streams.
+
+If libpkv.so is not built, every call raises: there is no fallback path.
+"""
+
+import torch
+
+from . import _lib
+from ._lib import NHD, HND, F16, BF16, E4M3, PkvError
+
+__all__ = [
+    "get_seq_lens",
+    "get_batch_indices_positions",
+    "csr_to_block_tables",
+    "append_paged_kv_cache",
+    "batch_prefill_with_kv_cache",
+    "batch_decode_with_kv_cache",
+    "prefill_workspace_size",
+    "decode_workspace_size",
+    "PkvError",
+]
+
+_DTYPES = {torch.float16: F16, torch.bfloat16: BF16, torch.float8_e4m3fn: E4M3}
+_LAYOUTS = {"NHD": NHD, "HND": HND}
+
+
+def _dt(t):
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {t.dtype}") from None
+
+
+def _layout(name):
+    try:
+        return _LAYOUTS[name]
+    except KeyError:
+        raise ValueError(f"kv_layout must be 'NHD' or 'HND', got {name!r}") from None
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _i32_on(t, device):
+    """int32 device copy of a length / index tensor (no copy if already so)."""
+    if not isinstance(t, torch.Tensor):
+        t = torch.as_tensor(t)
+    if t.dtype != torch.int32:
+        t = t.to(torch.int32)
+    return t.to(device).contiguous()
+
+
+def _split_cache(paged_kv_cache):
+    """(k, v, page_stride_k, page_stride_v) from a 5D tensor or a (k, v) tuple."""
+    if isinstance(paged_kv_cache, (tuple, list)):
+        k, v = paged_kv_cache
+    else:
+        if paged_kv_cache.dim() != 5 or paged_kv_cache.shape[1] != 2:
+            raise ValueError("a single paged_kv_cache tensor must be 5D with dim 1 == 2")
+        k, v = paged_kv_cache[:, 0], paged_kv_cache[:, 1]
+    for t in (k, v):
+        if t.dim() != 4:
+            raise ValueError("k/v caches must be 4D [pages, ., ., head_dim]")
+        inner = t.shape[1] * t.shape[2] * t.shape[3]
+        if (t.stride(3), t.stride(2), t.stride(1)) != (1, t.shape[3], t.shape[2] * t.shape[3]) \
+                or t.stride(0) < inner:
+            raise ValueError("each page of the k/v cache must be contiguous")
+    return k, v, k.stride(0), v.stride(0)
+
+
+def _cache_dims(k, layout):
+    """(page_size, num_kv_heads, head_dim) of a 4D cache view."""
+    if layout == NHD:
+        return k.shape[1], k.shape[2], k.shape[3]
+    return k.shape[2], k.shape[1], k.shape[3]
+
+
+def get_seq_lens(kv_indptr, kv_last_page_len, page_size):
+    """Tokens of each request: (pages - 1) * page_size + last_page_len."""
+    indptr = _i32_on(kv_indptr, kv_last_page_len.device)
+    last = _i32_on(kv_last_page_len, kv_last_page_len.device)
+    out = torch.empty(last.shape[0], dtype=torch.int32, device=last.device)
+    _lib.check(_lib.load().pkv_get_seq_lens(_ptr(indptr), _ptr(last), last.shape[0],
+                                            int(page_size), _ptr(out), _stream()),
+               "get_seq_lens")
+    return out
+
+
+def get_batch_indices_positions(append_indptr, seq_lens, nnz):
+    """(batch_indices, positions) of the appended rows; positions are the
+    last append-length positions of each request."""
+    ai = _i32_on(append_indptr, seq_lens.device)
+    seq = _i32_on(seq_lens, seq_lens.device)
+    bi = torch.empty(int(nnz), dtype=torch.int32, device=seq.device)
+    pos = torch.empty(int(nnz), dtype=torch.int32, device=seq.device)
+    _lib.check(_lib.load().pkv_get_batch_indices_positions(
+        _ptr(ai), _ptr(seq), seq.shape[0], int(nnz), _ptr(bi), _ptr(pos), _stream()),
+        "get_batch_indices_positions")
+    return bi, pos
+
+
+def csr_to_block_tables(kv_indptr, kv_indices, max_pages_per_seq):
+    """Dense block_tables [batch, max_pages_per_seq] from kv_indptr/kv_indices
+    (entries past a request's pages are -1)."""
+    indptr = _i32_on(kv_indptr, kv_indices.device)
+    idx = _i32_on(kv_indices, kv_indices.device)
+    batch = indptr.shape[0] - 1
+    bt = torch.empty(batch, int(max_pages_per_seq), dtype=torch.int32, device=idx.device)
+    _lib.check(_lib.load().pkv_csr_to_block_tables(
+        _ptr(indptr), _ptr(idx), batch, int(max_pages_per_seq), _ptr(bt), _stream()),
+        "csr_to_block_tables")
+    return bt
+
+
+def append_paged_kv_cache(append_key, append_value, batch_indices, positions,
+                          paged_kv_cache, kv_indices, kv_indptr, kv_last_page_len,
+                          kv_layout="NHD"):
+    """Scatter appended K/V rows into their pages (in place; returns None)."""
+    layout = _layout(kv_layout)
+    k, v, psk, psv = _split_cache(paged_kv_cache)
+    ps, hkv, d = _cache_dims(k, layout)
+    if append_key.dtype != k.dtype or append_value.dtype != k.dtype or v.dtype != k.dtype:
+        raise ValueError("append rows and cache must share one dtype")
+    if tuple(append_key.shape[1:]) != (hkv, d) or append_value.shape != append_key.shape:
+        raise ValueError("append_key/append_value must be [nnz, num_kv_heads, head_dim]")
+    ak, av = append_key.contiguous(), append_value.contiguous()
+    dev = k.device
+    bi, pos = _i32_on(batch_indices, dev), _i32_on(positions, dev)
+    idx, indptr = _i32_on(kv_indices, dev), _i32_on(kv_indptr, dev)
+    _lib.check(_lib.load().pkv_append_paged_kv_cache(
+        _ptr(ak), _ptr(av), _ptr(bi), _ptr(pos), ak.shape[0], _ptr(k), _ptr(v), psk, psv,
+        _ptr(idx), _ptr(indptr), None, indptr.shape[0] - 1, hkv, d, ps, layout, _dt(k),
+        _stream()), "append_paged_kv_cache")
+
+
+def prefill_workspace_size(batch_size):
+    return int(_lib.load().pkv_prefill_workspace_size(int(batch_size)))
+
+
+def _scale_ptr(x, device, keep):
+    if x is None:
+        return None
+    if not isinstance(x, torch.Tensor):
+        x = torch.tensor([float(x)], dtype=torch.float32, device=device)
+    if x.dtype != torch.float32 or x.numel() != 1:
+        raise ValueError("q/k/v scales must be float32 tensors with one element")
+    x = x.to(device).contiguous()
+    keep.append(x)
+    return x.data_ptr()
+
+
+def batch_prefill_with_kv_cache(q, k_cache, v_cache, scale, workspace_buffer, *,
+                                max_token_per_sequence, max_sequence_kv,
+                                actual_seq_lens_q, actual_seq_lens_kv, block_tables,
+                                causal, return_lse=True, q_scale=None, k_scale=None,
+                                v_scale=None, out=None, lse=None, o_data_type=None,
+                                kv_layout="HND"):
+    """Batch prefill over a paged cache; returns (out, lse)."""
+    if not return_lse:
+        raise ValueError("return_lse must be True")
+    layout = _layout(kv_layout)
+    dev = q.device
+    ps, hkv, d_qk = _cache_dims(k_cache, layout)
+    _, _, d_vo = _cache_dims(v_cache, layout)
+    for t in (k_cache, v_cache):
+        if t.dim() != 4 or t.stride(-1) != 1 or t.stride(-2) != t.shape[-1] or \
+                t.stride(1) != t.shape[2] * t.shape[3]:
+            raise ValueError("each page of k_cache/v_cache must be contiguous")
+    if q.dim() != 3 or q.shape[2] != d_qk:
+        raise ValueError("q must be [total_tokens, num_heads_qo, d_qk]")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q, k_cache and v_cache must share one dtype")
+    q = q.contiguous()
+    h_qo = q.shape[1]
+    if o_data_type is None:
+        o_data_type = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+    if out is None:
+        out = torch.empty(q.shape[0], h_qo, d_vo, dtype=o_data_type, device=dev)
+    if lse is None:
+        lse = torch.empty(q.shape[0], h_qo, dtype=torch.float32, device=dev)
+    if out.dtype != o_data_type or not out.is_contiguous() or tuple(out.shape) != (q.shape[0], h_qo, d_vo):
+        raise ValueError("out must be a contiguous [total_tokens, num_heads_qo, d_vo] tensor")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (q.shape[0], h_qo):
+        raise ValueError("lse must be a contiguous float32 [total_tokens, num_heads_qo] tensor")
+    lq = _i32_on(actual_seq_lens_q, dev)
+    lkv = _i32_on(actual_seq_lens_kv, dev)
+    bt = _i32_on(block_tables, dev)
+    keep = []
+    _lib.check(_lib.load().pkv_batch_prefill_with_kv_cache(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), k_cache.stride(0), v_cache.stride(0),
+        float(scale), _ptr(workspace_buffer), workspace_buffer.numel() * workspace_buffer.element_size(),
+        int(max_token_per_sequence), int(max_sequence_kv), _ptr(lq), _ptr(lkv), _ptr(bt),
+        bt.shape[1], lq.shape[0], h_qo, hkv, d_qk, d_vo, ps, layout, 1 if causal else 0,
+        _scale_ptr(q_scale, dev, keep), _scale_ptr(k_scale, dev, keep),
+        _scale_ptr(v_scale, dev, keep), _ptr(out), _ptr(lse), _dt(q), _dt(out), _stream()),
+        "batch_prefill_with_kv_cache")
+    return out, lse
+
+
+def decode_workspace_size(batch_size, q_len_per_req, num_heads_qo, num_heads_kv,
+                          head_dim, max_seq_len, window_left=-1):
+    return int(_lib.load().pkv_decode_workspace_size(
+        int(batch_size), int(q_len_per_req), int(num_heads_qo), int(num_heads_kv),
+        int(head_dim), int(max_seq_len), int(window_left)))
+
+
+def batch_decode_with_kv_cache(query, kv_cache, workspace_buffer, block_tables, seq_lens,
+                               max_seq_len, bmm1_scale=1.0, bmm2_scale=1.0, window_left=-1,
+                               out=None, out_dtype=None, sinks=None, kv_layout="HND",
+                               q_len_per_req=1):
+    """Batch decode over block_tables; returns out [num_tokens, num_heads, head_dim]."""
+    layout = _layout(kv_layout)
+    dev = query.device
+    k, v, psk, psv = _split_cache(kv_cache)
+    ps, hkv, d = _cache_dims(k, layout)
+    if query.dim() != 3 or query.shape[2] != d:
+        raise ValueError("query must be [num_tokens, num_heads, head_dim]")
+    query = query.contiguous()
+    h_qo = query.shape[1]
+    if query.shape[0] % int(q_len_per_req):
+        raise ValueError("num_tokens must be batch_size * q_len_per_req")
+    batch = query.shape[0] // int(q_len_per_req)
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else query.dtype
+    if out is None:
+        out = torch.empty(query.shape[0], h_qo, d, dtype=out_dtype, device=dev)
+    if out.dtype != out_dtype or not out.is_contiguous() or tuple(out.shape) != tuple(query.shape):
+        raise ValueError("out must be a contiguous tensor shaped like query")
+    bt = _i32_on(block_tables, dev)
+    seq = seq_lens.to(dev)
+    if seq.dtype not in (torch.int32, torch.uint32):
+        seq = seq.to(torch.int32)
+    seq = seq.contiguous()
+    if seq.shape[0] != batch:
+        raise ValueError("seq_lens must have batch_size entries")
+    sink_ptr = None
+    if sinks is not None:
+        if isinstance(sinks, (list, tuple)):
+            sinks = torch.cat([s.reshape(-1) for s in sinks])
+        sinks = sinks.to(device=dev, dtype=torch.float32).contiguous()
+        if sinks.numel() != h_qo:
+            raise ValueError("sinks must hold one value per qo head")
+        sink_ptr = sinks.data_ptr()
+    if isinstance(bmm1_scale, torch.Tensor) or isinstance(bmm2_scale, torch.Tensor):
+        raise ValueError("bmm1_scale / bmm2_scale must be Python floats here")
+    _lib.check(_lib.load().pkv_batch_decode_with_kv_cache(
+        _ptr(query), _ptr(k), _ptr(v), psk, psv, _ptr(workspace_buffer),
+        workspace_buffer.numel() * workspace_buffer.element_size(), _ptr(bt), bt.shape[1],
+        _ptr(seq), batch, int(max_seq_len), float(bmm1_scale), float(bmm2_scale),
+        int(window_left), _ptr(out), _dt(out), sink_ptr, layout, int(q_len_per_req), h_qo,
+        hkv, d, ps, _dt(query), _dt(k), _stream()), "batch_decode_with_kv_cache")
+    return out

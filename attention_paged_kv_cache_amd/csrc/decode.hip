@@ -1,0 +1,473 @@
+// Batch decode over a block_tables page table: split-KV on MFMA, LSE merge.
+//
+// Source: flashinfer.decode.trtllm_batch_decode_with_kv_cache -- Parameters
+// (query, kv_cache, workspace_buffer, block_tables, seq_lens, max_seq_len,
+// bmm1_scale, bmm2_scale, window_left, sinks, kv_layout, q_len_per_req).
+// Request b's q_len queries are its last q_len positions, causal among
+// themselves; window_left is an inclusive left window (-1: whole sequence);
+// a sink is a per-qo-head logit that joins only the softmax denominator.
+//
+// The kernel is bound by HBM reads of the K/V pages: every K and V element
+// of a kv head is read once and serves all G * q_len query rows of that
+// head (G = num_heads_qo / num_heads_kv). Those rows form the N side of
+// 16x16x32 MFMAs, so the arithmetic stays far below the matrix-core roof
+// and the loads decide the time.
+//
+// Work decomposition
+//   A unit is (request, kv head, split): `chunk` consecutive keys of the
+//   request's key range (only keys some query may see: with a window, the
+//   range starts at seq - q_len - window_left). A workgroup of 4 waves owns
+//   one unit; each wave streams chunk/4 keys, 32 at a time, straight from
+//   global memory into MFMA operands (no LDS on the streaming path):
+//     K: lane = (key, 8-element d run): 16-byte loads (8 bytes for e4m3,
+//        widened exactly to bf16 in registers).
+//     V: lane = (8 keys, 8-element d run): 8 loads, then an 8x8 transpose
+//        in registers gives V^T operands whose k-run is 8 consecutive keys.
+//     S^T = K Q^T, online softmax in fp32 (base 2), O^T += V^T P^T.
+//   The four waves' (m, l, O) are merged in LDS. A request that fits one
+//   unit writes its output directly; otherwise the unit writes its partial
+//   (m, l, O) to the workspace and a merge kernel combines the splits and
+//   the sink term.
+
+#include <math.h>
+
+#include <algorithm>
+
+#include "launch.h"
+#include "pkv_common.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kD = 128;
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c, BF16Tag) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c, F16Tag) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(
+      __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Eight e4m3fn codes -> eight 16-bit values of the query's type (exact).
+__device__ __forceinline__ u32x4 widen8(u32x2 w, BF16Tag) {
+  const u32x2 lo = e4m3x4_to_bf16x4(w[0]);
+  const u32x2 hi = e4m3x4_to_bf16x4(w[1]);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+__device__ __forceinline__ u32x4 widen8(u32x2 w, F16Tag) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[1], 1.0f, true));
+  return r;
+}
+
+// Load 8 consecutive d elements of one key row as a 16-byte operand.
+template <bool FP8, class QT>
+__device__ __forceinline__ u32x4 load_run(const char *p) {
+  if constexpr (FP8) {
+    return widen8(ld8(p), QT{});
+  } else {
+    return ld16(p);
+  }
+}
+
+__device__ __forceinline__ void key_range(const DecodeArgs &a, int seq, int &lo) {
+  lo = 0;
+  if (a.window_left >= 0) lo = max(0, seq - a.q_len - a.window_left);
+}
+
+// NB: number of 16-row blocks of the (q_len x G) query rows of a kv head.
+template <int NB, class QT, bool FP8>
+__global__ __launch_bounds__(kThreads, NB >= 3 ? 1 : 2) void decode_kernel(
+    DecodeArgs a, int32_t chunk, int32_t max_splits, float *__restrict__ ws_o,
+    float *__restrict__ ws_ml) {
+  constexpr int ES = FP8 ? 1 : 2;
+  constexpr int R = NB * 16;
+  __shared__ float sh_m[kWaves][R];
+  __shared__ float sh_l[kWaves][R];
+  __shared__ float sh_o[R][kD + 4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g4 = lane >> 4;
+  const int r16 = lane & 15;
+
+  const int bh = a.batch * a.num_heads_kv;
+  const int split = blockIdx.x / bh;
+  const int b = (blockIdx.x / a.num_heads_kv) % a.batch;
+  const int kvh = blockIdx.x % a.num_heads_kv;
+  const int seq = (int)a.seq_lens[b];
+  int lo;
+  key_range(a, seq, lo);
+  const int k_begin = lo + split * chunk;
+  if (k_begin >= seq) return;
+  const int k_end = min(seq, k_begin + chunk);
+  const int n_splits = (seq - lo + chunk - 1) / chunk;
+  const int cw = chunk / kWaves;
+  const int w_begin = k_begin + wave * cw;
+  const int w_end = min(k_end, w_begin + cw);
+
+  const int G = a.num_heads_qo / a.num_heads_kv;
+  const int rows = a.q_len * G;
+  const float c_raw = a.bmm1_scale * kLog2e;
+  const bool negate = c_raw < 0.0f;
+  const float c = fmaxf(fabsf(c_raw), 1e-30f);
+
+  // ---- Q^T operands: row n = 16*nb + r16 -> (query qi, head g) ------------
+  u32x4 qop[NB][4];
+  int pos[NB], wlo[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = nb * 16 + r16;
+    const int qi = n / G, g = n - qi * G;
+    const bool ok = n < rows;
+    pos[nb] = ok ? seq - a.q_len + qi : -1;  // last allowed key
+    wlo[nb] = (a.window_left >= 0) ? pos[nb] - a.window_left : 0;
+    const char *qp = (const char *)a.q +
+                     ((int64_t)(b * a.q_len + qi) * a.num_heads_qo + kvh * G + g) * kD * 2;
+    const uint32_t flip = negate ? 0x80008000u : 0u;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ok) v = ld16(qp + (s * 32 + g4 * 8) * 2);
+      v[0] ^= flip; v[1] ^= flip; v[2] ^= flip; v[3] ^= flip;
+      qop[nb][s] = v;
+    }
+  }
+  // bounds over the real rows only (padding rows have pos = -1)
+  int pos_min = 0x7fffffff, wlo_max = -0x7fffffff;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    if (nb * 16 + r16 < rows) {
+      pos_min = min(pos_min, pos[nb]);
+      wlo_max = max(wlo_max, wlo[nb]);
+    }
+  }
+  // wave-uniform bounds of the mask-free region
+  for (int off = 1; off < 64; off <<= 1) {
+    pos_min = min(pos_min, __shfl_xor(pos_min, off));
+    wlo_max = max(wlo_max, __shfl_xor(wlo_max, off));
+  }
+
+  const int *bt = a.block_tables + (int64_t)b * a.max_pages;
+  const int log2ps = __builtin_ctz(a.page_size);
+  const int ps_mask = a.page_size - 1;
+  const char *kbase = (const char *)a.k + (int64_t)kvh * a.head_stride * ES;
+  const char *vbase = (const char *)a.v + (int64_t)kvh * a.head_stride * ES;
+
+  f32x4 o[8][NB];
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[cc][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[NB], l_run[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    m_run[nb] = -INFINITY;
+    l_run[nb] = 0.0f;
+  }
+
+  for (int kg0 = w_begin; kg0 < w_end; kg0 += 32) {
+    // ---- gather K operands (two 16-key m-blocks, four 32-d k-steps) -------
+    u32x4 kop[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int key = kg0 + 8 * (r16 >> 2) + 4 * mb + (r16 & 3);
+      const bool ok = key < w_end;
+      const char *kp = kbase;
+      if (ok) {
+        const int page = bt[key >> log2ps];
+        kp += ((int64_t)page * a.page_stride_k + (int64_t)(key & ps_mask) * a.slot_stride) * ES;
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (ok) v = load_run<FP8, QT>(kp + (s * 32 + g4 * 8) * ES);
+        kop[mb][s] = v;
+      }
+    }
+    // ---- gather V: keys kg0 + 8*g4 + j, d run 8*r16 .. 8*r16+7 -----------
+    u32x4 vrow[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int key = kg0 + 8 * g4 + jj;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (key < w_end) {
+        const int page = bt[key >> log2ps];
+        const char *vp = vbase + ((int64_t)page * a.page_stride_v +
+                                  (int64_t)(key & ps_mask) * a.slot_stride) * ES;
+        v = load_run<FP8, QT>(vp + r16 * 8 * ES);
+      }
+      vrow[jj] = v;
+    }
+
+    // ---- S^T = K Q^T ---------------------------------------------------------
+    f32x4 sacc[2][NB];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mfma16(kop[mb][s], qop[nb][s], acc, QT{});
+        sacc[mb][nb] = acc;
+      }
+
+    // ---- mask where the group crosses a boundary -----------------------------
+    // lane holds keys kg0 + 8*g4 + 4*mb + i for its row
+    const bool clean = (kg0 + 32 <= w_end) && (kg0 >= wlo_max) && (kg0 + 31 <= pos_min);
+    if (!clean) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kg0 + 8 * g4 + 4 * mb + i;
+            if (key >= w_end || key > pos[nb] || key < wlo[nb]) sacc[mb][nb][i] = -INFINITY;
+          }
+    }
+
+    // ---- online softmax per row ------------------------------------------------
+    u32x4 pop[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sacc[mb][nb][i]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      const float m_new = fmaxf(m_run[nb], mloc * c);
+      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+      const float alpha = fast_exp2(m_run[nb] - m_use);
+      m_run[nb] = m_new;
+      float ps = 0.0f;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const float p0 = fast_exp2(fmaf(sacc[mb][nb][0], c, -m_use));
+        const float p1 = fast_exp2(fmaf(sacc[mb][nb][1], c, -m_use));
+        const float p2 = fast_exp2(fmaf(sacc[mb][nb][2], c, -m_use));
+        const float p3 = fast_exp2(fmaf(sacc[mb][nb][3], c, -m_use));
+        ps += (p0 + p1) + (p2 + p3);
+        pop[nb][2 * mb] = pack2(p0, p1, QT{});
+        pop[nb][2 * mb + 1] = pack2(p2, p3, QT{});
+      }
+      l_run[nb] = l_run[nb] * alpha + ps;
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) o[cc][nb] *= alpha;
+    }
+
+    // ---- O^T += V^T P^T ----------------------------------------------------------
+    u32x4 vt[8];
+    transpose8x8_b16(vrow, vt);
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) o[cc][nb] = mfma16(vt[cc], pop[nb], o[cc][nb], QT{});
+  }
+
+  // ---- merge the four waves ------------------------------------------------------
+  // lane (r16, g4) holds, for row 16*nb + r16: l partial over its keys and
+  // O^T at d = 8*(4*g4 + i) + cc.
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float l = l_run[nb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    l_run[nb] = l;
+    if (g4 == 0) {
+      sh_m[wave][nb * 16 + r16] = m_run[nb];
+      sh_l[wave][nb * 16 + r16] = l;
+    }
+  }
+  __syncthreads();
+  float fw[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = nb * 16 + r16;
+    float M = sh_m[0][n];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_m[w][n]);
+    const float M_use = (M == -INFINITY) ? 0.0f : M;
+    fw[nb] = fast_exp2(m_run[nb] - M_use);
+  }
+  // serialised accumulation keeps the summation order fixed
+  for (int w = 0; w < kWaves; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d = 8 * (4 * g4 + i) + cc;
+            const float v = o[cc][nb][i] * fw[nb];
+            float *dst = &sh_o[nb * 16 + r16][d];
+            *dst = (w == 0) ? v : *dst + v;
+          }
+    }
+    __syncthreads();
+  }
+
+  // ---- write: final output (single split) or partial ------------------------------
+  const int n_rows = rows;
+  const bool direct = n_splits == 1;
+  for (int idx = tid; idx < n_rows * (kD / 4); idx += kThreads) {
+    const int n = idx / (kD / 4);
+    const int d4 = (idx % (kD / 4)) * 4;
+    float M = sh_m[0][n];
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_m[w][n]);
+    const float M_use = (M == -INFINITY) ? 0.0f : M;
+    float L = 0.0f;
+    for (int w = 0; w < kWaves; ++w) L += sh_l[w][n] * fast_exp2(sh_m[w][n] - M_use);
+    const float *src = &sh_o[n][d4];
+    if (direct) {
+      const int qi = n / G, g = n - qi * G;
+      const int head = kvh * G + g;
+      float den = L;
+      if (a.sinks) den += fast_exp2(a.sinks[head] * kLog2e - M_use);
+      const float scale = den > 0.0f ? a.bmm2_scale / den : 0.0f;
+      char *op = (char *)a.out + ((int64_t)(b * a.q_len + qi) * a.num_heads_qo + head) * kD * 2;
+      u32x2 w;
+      if (a.out_dtype == 0) {
+        w[0] = pack2(src[0] * scale, src[1] * scale, F16Tag{});
+        w[1] = pack2(src[2] * scale, src[3] * scale, F16Tag{});
+      } else {
+        w[0] = pack2(src[0] * scale, src[1] * scale, BF16Tag{});
+        w[1] = pack2(src[2] * scale, src[3] * scale, BF16Tag{});
+      }
+      st8(op + d4 * 2, w);
+    } else {
+      const int64_t unit = ((int64_t)b * a.num_heads_kv + kvh) * max_splits + split;
+      float *dst = ws_o + (unit * rows + n) * kD + d4;
+      *reinterpret_cast<f32x4 *>(dst) = f32x4{src[0], src[1], src[2], src[3]};
+      if (d4 == 0) {
+        ws_ml[(unit * rows + n) * 2 + 0] = M;
+        ws_ml[(unit * rows + n) * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// One wave per (request, kv head, row); lanes cover d in pairs.
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a,
+                                                           int32_t chunk,
+                                                           int32_t max_splits,
+                                                           const float *__restrict__ ws_o,
+                                                           const float *__restrict__ ws_ml) {
+  const int G = a.num_heads_qo / a.num_heads_kv;
+  const int rows = a.q_len * G;
+  const int gw = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int total = a.batch * a.num_heads_kv * rows;
+  if (gw >= total) return;
+  const int n = gw % rows;
+  const int kvh = (gw / rows) % a.num_heads_kv;
+  const int b = gw / (rows * a.num_heads_kv);
+  const int seq = (int)a.seq_lens[b];
+  int lo;
+  key_range(a, seq, lo);
+  const int n_splits = seq > lo ? (seq - lo + chunk - 1) / chunk : 0;
+  const int qi = n / G, g = n - qi * G;
+  const int head = kvh * G + g;
+  char *op = (char *)a.out + ((int64_t)(b * a.q_len + qi) * a.num_heads_qo + head) * kD * 2;
+  if (n_splits == 1) return;  // written by the split kernel
+  const int64_t unit0 = ((int64_t)b * a.num_heads_kv + kvh) * max_splits;
+  float M = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, ws_ml[((unit0 + s) * rows + n) * 2]);
+  const float sink = a.sinks ? a.sinks[head] * kLog2e : -INFINITY;
+  const float M_all = fmaxf(M, sink);
+  const float M_use = (M_all == -INFINITY) ? 0.0f : M_all;
+  float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  for (int s = 0; s < n_splits; ++s) {
+    const int64_t u = (unit0 + s) * rows + n;
+    const float f = fast_exp2(ws_ml[u * 2] - M_use);
+    L += f * ws_ml[u * 2 + 1];
+    const f32x2 v = *reinterpret_cast<const f32x2 *>(ws_o + u * kD + lane * 2);
+    o0 += f * v[0];
+    o1 += f * v[1];
+  }
+  if (a.sinks) L += fast_exp2(sink - M_use);
+  const float scale = L > 0.0f ? a.bmm2_scale / L : 0.0f;
+  uint32_t w = (a.out_dtype == 0) ? pack2(o0 * scale, o1 * scale, F16Tag{})
+                                  : pack2(o0 * scale, o1 * scale, BF16Tag{});
+  *reinterpret_cast<uint32_t *>(op + lane * 4) = w;
+}
+
+template <int NB, class QT, bool FP8>
+hipError_t launch_nb(const DecodeArgs &a, const DecodePlan &p, hipStream_t s) {
+  float *ws = reinterpret_cast<float *>(a.workspace);
+  const int64_t units = (int64_t)a.batch * a.num_heads_kv;
+  float *ws_o = ws;
+  float *ws_ml = ws + units * p.max_splits * p.rows * kD;
+  const int64_t blocks = units * p.max_splits;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((decode_kernel<NB, QT, FP8>), dim3((uint32_t)blocks),
+                     dim3(kThreads), 0, s, a, p.chunk, p.max_splits, ws_o, ws_ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.max_splits == 1) return e;
+  const int64_t waves = units * p.rows;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((uint32_t)((waves + 3) / 4)),
+                     dim3(256), 0, s, a, p.chunk, p.max_splits, ws_o, ws_ml);
+  return hipGetLastError();
+}
+
+template <class QT, bool FP8>
+hipError_t launch_q(const DecodeArgs &a, const DecodePlan &p, hipStream_t s) {
+  switch ((p.rows + 15) / 16) {
+    case 1: return launch_nb<1, QT, FP8>(a, p, s);
+    case 2: return launch_nb<2, QT, FP8>(a, p, s);
+    case 3: return launch_nb<3, QT, FP8>(a, p, s);
+    default: return launch_nb<4, QT, FP8>(a, p, s);
+  }
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int32_t batch, int32_t q_len, int32_t num_heads_qo,
+                       int32_t num_heads_kv, int32_t head_dim,
+                       int32_t max_seq_len, int32_t window_left) {
+  DecodePlan p{};
+  const int G = num_heads_qo / num_heads_kv;
+  p.rows = q_len * G;
+  const int64_t max_keys =
+      window_left >= 0 ? (int64_t)std::min<int64_t>(max_seq_len, (int64_t)window_left + q_len)
+                       : (int64_t)max_seq_len;
+  const int64_t units = (int64_t)batch * num_heads_kv;
+  // Enough workgroups to fill the chip, but chunks long enough that the
+  // partial (m, l, O) rows stay a small fraction of the K/V bytes.
+  int64_t c_bal = units > 0 ? (max_keys * units + 16383) / 16384 : max_keys;
+  const int64_t kv_bytes_per_key = 2 * (int64_t)head_dim;  // one byte per element at least
+  int64_t c_min = 20 * (int64_t)p.rows * (head_dim + 2) * 4 / kv_bytes_per_key;
+  int64_t chunk = std::max<int64_t>(c_bal, c_min);
+  chunk = std::max<int64_t>(chunk, 128);
+  chunk = (chunk + 127) / 128 * 128;
+  const int64_t cap = (max_keys + 127) / 128 * 128;
+  if (chunk > cap) chunk = std::max<int64_t>(cap, 128);
+  p.chunk = (int32_t)chunk;
+  p.max_splits = max_keys > 0 ? (int32_t)((max_keys + chunk - 1) / chunk) : 1;
+  p.workspace_bytes = p.max_splits > 1
+                          ? (size_t)units * p.max_splits * p.rows * (kD + 2) * sizeof(float)
+                          : 0;
+  return p;
+}
+
+hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &p, hipStream_t s) {
+  const bool fp8 = a.kv_dtype == 2;
+  const bool f16 = a.q_dtype == 0;
+  if (fp8) return f16 ? launch_q<F16Tag, true>(a, p, s) : launch_q<BF16Tag, true>(a, p, s);
+  return f16 ? launch_q<F16Tag, false>(a, p, s) : launch_q<BF16Tag, false>(a, p, s);
+}
+
+}  // namespace pkv

@@ -1,0 +1,91 @@
+// Host-side launchers of the HIP kernels. Declared here, defined next to
+// their kernels, called from the C ABI layer after validation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+hipError_t launch_get_seq_lens(const int32_t *kv_indptr, const int32_t *last,
+                               int32_t batch, int32_t page_size,
+                               int32_t *seq_lens, hipStream_t s);
+
+hipError_t launch_batch_indices_positions(const int32_t *append_indptr,
+                                          const int32_t *seq_lens,
+                                          int32_t batch, int32_t nnz,
+                                          int32_t *batch_indices,
+                                          int32_t *positions, hipStream_t s);
+
+hipError_t launch_csr_to_block_tables(const int32_t *kv_indptr,
+                                      const int32_t *kv_indices, int32_t batch,
+                                      int32_t max_pages, int32_t *bt,
+                                      hipStream_t s);
+
+struct AppendArgs {
+  const void *key, *value;
+  const int32_t *batch_indices, *positions;
+  int32_t nnz;
+  void *k_cache, *v_cache;
+  int64_t page_stride_k, page_stride_v;  // bytes
+  int64_t slot_stride, head_stride;      // bytes
+  const int32_t *kv_indices, *kv_indptr;
+  int32_t num_heads, row_bytes_per_head;  // bytes of one head's head_dim run
+  int32_t page_size;
+};
+hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+
+// Exclusive prefix sum of lens[0..batch) into out[0..batch].
+hipError_t launch_exclusive_cumsum(const int32_t *lens, int32_t batch,
+                                   int32_t *out, hipStream_t s);
+
+struct PrefillArgs {
+  const void *q, *k, *v;
+  int64_t page_stride_k, page_stride_v;  // elements
+  int64_t slot_stride_k, head_stride_k;  // elements
+  int64_t slot_stride_v, head_stride_v;  // elements
+  const int32_t *lens_q, *lens_kv, *cum_q;
+  const int32_t *block_tables;
+  int32_t max_pages;
+  int32_t batch, num_heads_qo, num_heads_kv, d_qk, d_vo, page_size;
+  int32_t max_q;
+  int32_t causal;
+  float scale;
+  const float *q_scale, *k_scale, *v_scale;
+  void *out;
+  float *lse;
+  int32_t qkv_dtype, o_dtype;  // pkv_dtype values
+};
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+
+struct DecodeArgs {
+  const void *q, *k, *v;
+  int64_t page_stride_k, page_stride_v;  // elements
+  int64_t slot_stride, head_stride;      // elements
+  const int32_t *block_tables;
+  int32_t max_pages;
+  const uint32_t *seq_lens;
+  int32_t batch, max_seq_len;
+  float bmm1_scale, bmm2_scale;
+  int32_t window_left;
+  void *out;
+  const float *sinks;
+  int32_t q_len, num_heads_qo, num_heads_kv, head_dim, page_size;
+  int32_t q_dtype, kv_dtype, out_dtype;  // pkv_dtype values
+  void *workspace;
+};
+// Split plan shared by the workspace-size query and the launcher.
+struct DecodePlan {
+  int32_t rows;        // q_len * G, rows per (request, kv head)
+  int32_t chunk;       // keys per split
+  int32_t max_splits;  // splits per (request, kv head), upper bound
+  size_t workspace_bytes;
+};
+DecodePlan plan_decode(int32_t batch, int32_t q_len, int32_t num_heads_qo,
+                       int32_t num_heads_kv, int32_t head_dim,
+                       int32_t max_seq_len, int32_t window_left);
+hipError_t launch_decode(const DecodeArgs &a, const DecodePlan &plan,
+                         hipStream_t s);
+
+}  // namespace pkv

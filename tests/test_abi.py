@@ -1,0 +1,132 @@
+"""The C ABI library loads, exports every symbol include/pkv.h declares, and
+rejects bad arguments on the host before any HIP call (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+from attention_paged_kv_cache_amd import _lib
+
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libpkv.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_abi_version(lib):
+    assert lib.pkv_abi_version() == 1
+
+
+def _err(lib):
+    return lib.pkv_last_error().decode()
+
+
+# Pointers below are never dereferenced: every call must fail validation.
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def _prefill(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, psk=16 * 8 * 128, psv=16 * 8 * 128, scale=0.1,
+             ws=FAKE, ws_bytes=4096, max_q=10, max_kv=10, lq=FAKE, lkv=FAKE, bt=FAKE,
+             max_pages=1, batch=1, hqo=32, hkv=8, dqk=128, dvo=128, ps=16, layout=1,
+             causal=1, qs=None, ks=None, vs=None, out=FAKE, lse=FAKE, qdt=1, odt=1,
+             stream=None)
+    a.update(over)
+    return lib.pkv_batch_prefill_with_kv_cache(*a.values())
+
+
+@pytest.mark.parametrize("over,needle", [
+    (dict(dqk=64), "128 or 192"),
+    (dict(dvo=192), "must be 128"),
+    (dict(hqo=4, hkv=8), ">= num_heads_kv"),
+    (dict(hqo=12, hkv=8), "multiple"),
+    (dict(lse=None), "lse is required"),
+    (dict(layout=7), "NHD or HND"),
+    (dict(ps=8), "page_size"),
+    (dict(ws_bytes=0), "workspace"),
+    (dict(odt=2), "output dtype"),
+    (dict(batch=-1), "batch_size"),
+    (dict(psk=100), "page stride"),
+    (dict(max_kv=17), "too narrow"),
+])
+def test_prefill_validation(lib, over, needle):
+    st = _prefill(lib, **over)
+    assert st in (1, 2, 3)
+    assert needle in _err(lib)
+
+
+def _decode(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, psk=2 * 16 * 8 * 128, psv=2 * 16 * 8 * 128, ws=FAKE,
+             ws_bytes=1 << 30, bt=FAKE, max_pages=64, seq=FAKE, batch=4, max_seq=1024,
+             bmm1=0.1, bmm2=1.0, window=-1, out=FAKE, odt=1, sinks=None, layout=1, ql=1,
+             hqo=32, hkv=8, d=128, ps=16, qdt=1, kvdt=1, stream=None)
+    a.update(over)
+    return lib.pkv_batch_decode_with_kv_cache(*a.values())
+
+
+@pytest.mark.parametrize("over,needle", [
+    (dict(window=-2), "window_left"),
+    (dict(ql=0), "q_len_per_req"),
+    (dict(d=64), "head_dim"),
+    (dict(ql=3, hqo=32, hkv=1), "<= 64"),
+    (dict(qdt=2), "query dtype"),
+    (dict(kvdt=0), "kv dtype"),
+    (dict(ws_bytes=0, max_seq=100000, max_pages=10000), "workspace"),
+    (dict(layout=3), "NHD or HND"),
+    (dict(max_pages=1), "too narrow"),
+    (dict(hqo=8, hkv=16), ">= num_heads_kv"),
+])
+def test_decode_validation(lib, over, needle):
+    st = _decode(lib, **over)
+    assert st in (1, 2, 3)
+    assert needle in _err(lib)
+
+
+def test_append_validation(lib):
+    st = lib.pkv_append_paged_kv_cache(FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, 100, 100, FAKE,
+                                       FAKE, None, 1, 32, 128, 16, 0, 0, None)
+    assert st == 1 and "page stride" in _err(lib)
+    st = lib.pkv_append_paged_kv_cache(FAKE, FAKE, FAKE, FAKE, 10, FAKE, FAKE, 1 << 20, 1 << 20,
+                                       FAKE, FAKE, None, 1, 32, 4, 16, 0, 0, None)
+    assert st == 2 and "16 bytes" in _err(lib)
+    st = lib.pkv_append_paged_kv_cache(FAKE, FAKE, FAKE, FAKE, -1, FAKE, FAKE, 1 << 20, 1 << 20,
+                                       FAKE, FAKE, None, 1, 32, 128, 16, 0, 0, None)
+    assert st == 1 and "nnz" in _err(lib)
+
+
+def test_index_validation(lib):
+    assert lib.pkv_get_seq_lens(FAKE, FAKE, 4, 0, FAKE, None) == 1
+    assert lib.pkv_get_batch_indices_positions(FAKE, FAKE, 4, -3, FAKE, FAKE, None) == 1
+    assert lib.pkv_csr_to_block_tables(FAKE, FAKE, 4, 0, FAKE, None) == 1
+    # empty work is not an error and enqueues nothing
+    assert lib.pkv_get_seq_lens(None, None, 0, 16, None, None) == 0
+
+
+def test_workspace_sizes(lib):
+    assert lib.pkv_prefill_workspace_size(16) >= 17 * 4
+    # cfg-like decode sizes stay within the 128 MB the prefill page suggests
+    assert 0 < lib.pkv_decode_workspace_size(256, 1, 32, 8, 128, 8192, -1) < 128 << 20
+    assert 0 < lib.pkv_decode_workspace_size(64, 4, 64, 8, 128, 32768, 4095) < 128 << 20
+    assert lib.pkv_decode_workspace_size(4, 0, 32, 8, 128, 1024, -1) == 0

@@ -1,0 +1,157 @@
+"""GPU parity of batch decode (and append followed by decode) against the
+float64 oracle. Bar: |out - ref| <= 2e-2 + half an output ulp of ref."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.helpers import assert_out_close, bits, oracle_decode
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import attention_paged_kv_cache_amd as m
+    return m
+
+
+def run_decode(pkv, w, kv_cache=None):
+    kv = w["kv_cache"] if kv_cache is None else kv_cache
+    ws = torch.zeros(max(pkv.decode_workspace_size(
+        w["seq_lens"].shape[0], w["q_len_per_req"], w["num_qo_heads"], w["num_kv_heads"],
+        w["head_dim"], w["max_seq_len"], w["window_left"]), 16), dtype=torch.uint8, device=DEV)
+    sinks = None if w["sinks"] is None else w["sinks"].to(DEV)
+    out = pkv.batch_decode_with_kv_cache(
+        w["query"], kv, ws, w["block_tables"].to(DEV), w["seq_lens"].to(DEV), w["max_seq_len"],
+        bmm1_scale=w["bmm1_scale"], bmm2_scale=w["bmm2_scale"], window_left=w["window_left"],
+        sinks=sinks, kv_layout=w["layout"], q_len_per_req=w["q_len_per_req"])
+    torch.cuda.synchronize()
+    return out
+
+
+def check(pkv, w, requests=None):
+    out = run_decode(pkv, w)
+    ref = oracle_decode(w, requests)
+    if requests is not None:
+        ql = w["q_len_per_req"]
+        idx = torch.tensor([b * ql + i for b in requests for i in range(ql)], device=DEV)
+        out = out.index_select(0, idx)
+    err = assert_out_close(out, ref, out.dtype)
+    print(f"max |out err| {err:.3g}", flush=True)
+    return out
+
+
+def small(**kw):
+    args = dict(device=DEV, seed=40, batch=5, seq=(1, 700))
+    args.update(kw)
+    return workloads.batch_decode(**args)
+
+
+@pytest.mark.parametrize("hqo,hkv", [(32, 8), (8, 8), (16, 1)])
+def test_bf16(pkv, hqo, hkv):
+    check(pkv, small(num_qo_heads=hqo, num_kv_heads=hkv, seed=hqo + hkv))
+
+
+@pytest.mark.parametrize("ps,layout", [(16, "NHD"), (32, "HND"), (64, "NHD")])
+def test_layouts_and_pages(pkv, ps, layout):
+    check(pkv, small(page_size=ps, layout=layout, seed=ps))
+
+
+def test_long_sequences_split_kv(pkv):
+    # long enough that every request needs several splits
+    check(pkv, small(batch=3, seq=(3000, 9000), seed=41))
+
+
+@pytest.mark.parametrize("ql,window,sinks", [(4, 100, True), (2, -1, True), (4, 0, False),
+                                             (3, 37, False), (1, 5000, True)])
+def test_multi_query_window_sinks(pkv, ql, window, sinks):
+    check(pkv, small(q_len_per_req=ql, window_left=window, sinks=sinks, num_qo_heads=16,
+                     num_kv_heads=2, seq=(1, 900), seed=50 + ql))
+
+
+def test_fp8_kv(pkv):
+    w = small(kv_dtype=torch.float8_e4m3fn, q_len_per_req=4, window_left=200, sinks=True,
+              num_qo_heads=16, num_kv_heads=2, page_size=32, seed=42)
+    w["bmm1_scale"], w["bmm2_scale"] = 0.7 / np.sqrt(128), 1.3
+    check(pkv, w)
+
+
+def test_rows_64(pkv):
+    # q_len * G = 64, the largest supported row count per kv head
+    check(pkv, small(q_len_per_req=4, num_qo_heads=16, num_kv_heads=1, seq=(100, 2000),
+                     seed=43))
+
+
+def test_seq_shorter_than_q_len(pkv):
+    w = small(q_len_per_req=4, num_qo_heads=4, num_kv_heads=4, seed=44, batch=3, seq=(1, 3))
+    check(pkv, w)
+
+
+def test_e4m3_decode_table_exhaustive(pkv):
+    # seq_len 1 and q = 0: the output is bmm2 * v[0] exactly, so V rows
+    # holding all 256 codes read back the GPU's e4m3fn decode (bf16 holds
+    # every e4m3fn value exactly). NaN codes must come back NaN.
+    B, H, D, ps = 2, 1, 128, 16
+    kv = torch.zeros(B, 2, H, ps, D, dtype=torch.uint8, device=DEV)
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).reshape(2, 128)
+    kv[:, 1, 0, 0, :] = codes.to(DEV)
+    kv = kv.view(torch.float8_e4m3fn)
+    q = torch.zeros(B, H, D, dtype=torch.bfloat16, device=DEV)
+    bt = torch.arange(B, dtype=torch.int32).reshape(B, 1)
+    w = dict(query=q, kv_cache=kv, block_tables=bt,
+             seq_lens=torch.ones(B, dtype=torch.int32).to(torch.uint32), max_seq_len=1,
+             page_size=ps, num_qo_heads=H, num_kv_heads=H, head_dim=D, q_len_per_req=1,
+             bmm1_scale=1.0, bmm2_scale=1.0, window_left=-1, sinks=None, layout="HND")
+    out = run_decode(pkv, w).float().cpu().numpy().reshape(256).astype(np.float64)
+    tab = oracle.e4m3fn_table()
+    assert np.array_equal(np.isnan(out), np.isnan(tab))
+    ok = ~np.isnan(tab)
+    assert np.array_equal(out[ok], tab[ok])
+
+
+def test_deterministic(pkv):
+    w = small(seed=45, seq=(2000, 5000), q_len_per_req=2, sinks=True)
+    a = run_decode(pkv, w)
+    b = run_decode(pkv, w)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_full_size_bf16_sampled(pkv):
+    w = workloads.batch_decode(DEV)
+    out = run_decode(pkv, w)
+    assert torch.isfinite(out.float()).all()
+    reqs = [0, 7, 100, int(torch.argmax(w["seq_lens"].to(torch.int64))),
+            int(torch.argmin(w["seq_lens"].to(torch.int64)))]
+    ref = oracle_decode(w, reqs)
+    assert_out_close(out.index_select(0, torch.tensor(reqs, device=DEV)), ref, out.dtype)
+
+
+def test_full_size_append_then_spec_decode_sampled(pkv):
+    w = workloads.spec_decode(DEV)
+    kv = w["kv_cache"]
+    seq = w["seq_lens"].to(torch.int32).to(DEV)
+    bi, pos = pkv.get_batch_indices_positions(w["append_indptr"].to(DEV), seq,
+                                              w["k_append"].shape[0])
+    pkv.append_paged_kv_cache(w["k_append"], w["v_append"], bi, pos, kv,
+                              w["kv_indices"].to(DEV), w["kv_indptr"].to(DEV),
+                              w["kv_last_page_len"].to(DEV), kv_layout="HND")
+    out = run_decode(pkv, w)
+    assert torch.isfinite(out.float()).all()
+    reqs = [0, 9, 33, 63]
+    ref = oracle_decode(w, reqs)
+    idx = torch.tensor([b * 4 + i for b in reqs for i in range(4)], device=DEV)
+    assert_out_close(out.index_select(0, idx), ref, out.dtype)
+    # the appended rows are what the last 4 positions of each request hold
+    b = 9
+    L = int(w["seq_lens"][b])
+    ps = w["page_size"]
+    for i in range(4):
+        p = L - 4 + i
+        page = int(w["block_tables"][b, p // ps])
+        assert torch.equal(kv[page, 0, :, p % ps].view(torch.uint8),
+                           w["k_append"][b * 4 + i].view(torch.uint8))
