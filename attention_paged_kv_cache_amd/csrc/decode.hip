@@ -32,6 +32,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "launch.h"
 #include "pkv_common.h"
@@ -79,14 +80,27 @@ __device__ __forceinline__ u32x4 load_run(const char *p) {
   }
 }
 
-__device__ __forceinline__ void key_range(const DecodeArgs &a, int seq, int &lo) {
-  lo = 0;
+// First key a unit range may start at: the window's left edge (if any),
+// rounded down to a multiple of 32 so that every 32-key step starts on a
+// page boundary for page sizes 16, 32 and 64. Keys below the true left edge
+// are masked like any other key outside the window.
+__device__ __forceinline__ int key_origin(const DecodeArgs &a, int seq) {
+  int lo = 0;
   if (a.window_left >= 0) lo = max(0, seq - a.q_len - a.window_left);
+  return lo & ~31;
 }
+
+// Raw K/V of one 32-key step as loaded (e4m3 bytes or 16-bit values).
+template <bool FP8>
+struct RawKV {
+  using T = typename std::conditional<FP8, u32x2, u32x4>::type;
+  T k[2][4];  // [m-block][32-d k-step]
+  T v[8];     // 8 keys x 8 d
+};
 
 // NB: number of 16-row blocks of the (q_len x G) query rows of a kv head.
 template <int NB, class QT, bool FP8>
-__global__ __launch_bounds__(kThreads, NB >= 3 ? 1 : 2) void decode_kernel(
+__global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) void decode_kernel(
     DecodeArgs a, int32_t chunk, int32_t max_splits, float *__restrict__ ws_o,
     float *__restrict__ ws_ml) {
   constexpr int ES = FP8 ? 1 : 2;
@@ -97,7 +111,7 @@ __global__ __launch_bounds__(kThreads, NB >= 3 ? 1 : 2) void decode_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4;
   const int r16 = lane & 15;
 
@@ -106,8 +120,7 @@ __global__ __launch_bounds__(kThreads, NB >= 3 ? 1 : 2) void decode_kernel(
   const int b = (blockIdx.x / a.num_heads_kv) % a.batch;
   const int kvh = blockIdx.x % a.num_heads_kv;
   const int seq = (int)a.seq_lens[b];
-  int lo;
-  key_range(a, seq, lo);
+  const int lo = key_origin(a, seq);
   const int k_begin = lo + split * chunk;
   if (k_begin >= seq) return;
   const int k_end = min(seq, k_begin + chunk);
@@ -157,12 +170,53 @@ __global__ __launch_bounds__(kThreads, NB >= 3 ? 1 : 2) void decode_kernel(
     pos_min = min(pos_min, __shfl_xor(pos_min, off));
     wlo_max = max(wlo_max, __shfl_xor(wlo_max, off));
   }
+  pos_min = __builtin_amdgcn_readfirstlane(pos_min);
+  wlo_max = __builtin_amdgcn_readfirstlane(wlo_max);
 
-  const int *bt = a.block_tables + (int64_t)b * a.max_pages;
+  const int32_t *__restrict__ bt = a.block_tables + (int64_t)b * a.max_pages;
   const int log2ps = __builtin_ctz(a.page_size);
   const int ps_mask = a.page_size - 1;
+  const int last_pg = (seq - 1) >> log2ps;
   const char *kbase = (const char *)a.k + (int64_t)kvh * a.head_stride * ES;
   const char *vbase = (const char *)a.v + (int64_t)kvh * a.head_stride * ES;
+  const int64_t psk = a.page_stride_k * ES, psv = a.page_stride_v * ES;
+  const int64_t sstr = a.slot_stride * ES;
+
+  // Per-lane key offsets inside a 32-key step (loop invariant).
+  //   K, m-block mb: offset 8*(r16/4) + 4*mb + r16%4 (the lane's MFMA row)
+  //   V: offsets 8*g4 .. 8*g4+7 (the lane's 8-key run)
+  int koff[2];
+  koff[0] = 8 * (r16 >> 2) + (r16 & 3);
+  koff[1] = koff[0] + 4;
+  const int voff = 8 * g4;
+
+  // The two pages a 32-key step can touch (the second differs only for
+  // 16-token pages); indices are clamped into the sequence so that no
+  // padding entry of the block table is ever followed.
+  auto step_pages = [&](int kg0, int &p0, int &p1) {
+    p0 = bt[min(kg0 >> log2ps, last_pg)];
+    p1 = bt[min((kg0 + 16) >> log2ps, last_pg)];
+  };
+  auto issue = [&](RawKV<FP8> &r, int kg0, int p0, int p1) {
+    const char *kb0 = kbase + (int64_t)p0 * psk, *kb1 = kbase + (int64_t)p1 * psk;
+    const char *vb0 = vbase + (int64_t)p0 * psv, *vb1 = vbase + (int64_t)p1 * psv;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int off = koff[mb];
+      const char *kp = ((off >> log2ps) ? kb1 : kb0) + ((kg0 + off) & ps_mask) * sstr + g4 * 8 * ES;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if constexpr (FP8) r.k[mb][s] = ld8(kp + s * 32 * ES);
+        else r.k[mb][s] = ld16(kp + s * 32 * ES);
+      }
+    }
+    const char *vp = ((voff >> log2ps) ? vb1 : vb0) + ((kg0 + voff) & ps_mask) * sstr + r16 * 8 * ES;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if constexpr (FP8) r.v[jj] = ld8(vp + jj * sstr);
+      else r.v[jj] = ld16(vp + jj * sstr);
+    }
+  };
 
   f32x4 o[8][NB];
 #pragma unroll
@@ -176,41 +230,29 @@ __global__ __launch_bounds__(kThreads, NB >= 3 ? 1 : 2) void decode_kernel(
     l_run[nb] = 0.0f;
   }
 
-  for (int kg0 = w_begin; kg0 < w_end; kg0 += 32) {
-    // ---- gather K operands (two 16-key m-blocks, four 32-d k-steps) -------
-    u32x4 kop[2][4];
+  auto compute = [&](const RawKV<FP8> &r, int kg0) {
+    u32x4 kop[2][4], vrow[8];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int key = kg0 + 8 * (r16 >> 2) + 4 * mb + (r16 & 3);
-      const bool ok = key < w_end;
-      const char *kp = kbase;
-      if (ok) {
-        const int page = bt[key >> log2ps];
-        kp += ((int64_t)page * a.page_stride_k + (int64_t)(key & ps_mask) * a.slot_stride) * ES;
-      }
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (ok) v = load_run<FP8, QT>(kp + (s * 32 + g4 * 8) * ES);
-        kop[mb][s] = v;
+        if constexpr (FP8) kop[mb][s] = widen8(r.k[mb][s], QT{});
+        else kop[mb][s] = r.k[mb][s];
       }
-    }
-    // ---- gather V: keys kg0 + 8*g4 + j, d run 8*r16 .. 8*r16+7 -----------
-    u32x4 vrow[8];
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
-      const int key = kg0 + 8 * g4 + jj;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (key < w_end) {
-        const int page = bt[key >> log2ps];
-        const char *vp = vbase + ((int64_t)page * a.page_stride_v +
-                                  (int64_t)(key & ps_mask) * a.slot_stride) * ES;
-        v = load_run<FP8, QT>(vp + r16 * 8 * ES);
-      }
-      vrow[jj] = v;
+      if constexpr (FP8) vrow[jj] = widen8(r.v[jj], QT{});
+      else vrow[jj] = r.v[jj];
+    }
+    // keys past the sequence end hold whatever the last page's tail holds:
+    // zero them so that p = 0 meets v = 0, never NaN
+    if (kg0 + 32 > seq) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        if (kg0 + voff + jj >= seq) vrow[jj] = u32x4{0u, 0u, 0u, 0u};
     }
 
-    // ---- S^T = K Q^T ---------------------------------------------------------
+    // ---- S^T = K Q^T -------------------------------------------------------
     f32x4 sacc[2][NB];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -222,9 +264,10 @@ __global__ __launch_bounds__(kThreads, NB >= 3 ? 1 : 2) void decode_kernel(
         sacc[mb][nb] = acc;
       }
 
-    // ---- mask where the group crosses a boundary -----------------------------
+    // ---- mask where the step crosses a boundary ----------------------------
     // lane holds keys kg0 + 8*g4 + 4*mb + i for its row
-    const bool clean = (kg0 + 32 <= w_end) && (kg0 >= wlo_max) && (kg0 + 31 <= pos_min);
+    const bool clean = (kg0 + 32 <= w_end) && (kg0 >= w_begin) && (kg0 >= wlo_max) &&
+                       (kg0 + 31 <= pos_min);
     if (!clean) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -233,11 +276,12 @@ __global__ __launch_bounds__(kThreads, NB >= 3 ? 1 : 2) void decode_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = kg0 + 8 * g4 + 4 * mb + i;
-            if (key >= w_end || key > pos[nb] || key < wlo[nb]) sacc[mb][nb][i] = -INFINITY;
+            if (key >= w_end || key < w_begin || key > pos[nb] || key < wlo[nb])
+              sacc[mb][nb][i] = -INFINITY;
           }
     }
 
-    // ---- online softmax per row ------------------------------------------------
+    // ---- online softmax per row ----------------------------------------------
     u32x4 pop[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -268,13 +312,43 @@ __global__ __launch_bounds__(kThreads, NB >= 3 ? 1 : 2) void decode_kernel(
       for (int cc = 0; cc < 8; ++cc) o[cc][nb] *= alpha;
     }
 
-    // ---- O^T += V^T P^T ----------------------------------------------------------
+    // ---- O^T += V^T P^T --------------------------------------------------------
     u32x4 vt[8];
     transpose8x8_b16(vrow, vt);
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) o[cc][nb] = mfma16(vt[cc], pop[nb], o[cc][nb], QT{});
+  };
+
+  // ---- stream the wave's keys: loads of step i+1 fly during step i --------
+  // Two named buffers (no register copies); page ids are fetched one step
+  // ahead of the loads that use them.
+  if (w_begin < w_end) {
+    RawKV<FP8> buf_a, buf_b;
+    int p0, p1, n0, n1;
+    step_pages(w_begin, p0, p1);
+    issue(buf_a, w_begin, p0, p1);
+    step_pages(w_begin + 32, n0, n1);
+    int kg = w_begin;
+    while (true) {
+      bool more = kg + 32 < w_end;
+      if (more) {
+        issue(buf_b, kg + 32, n0, n1);
+        step_pages(kg + 64, n0, n1);
+      }
+      compute(buf_a, kg);
+      kg += 32;
+      if (!more) break;
+      more = kg + 32 < w_end;
+      if (more) {
+        issue(buf_a, kg + 32, n0, n1);
+        step_pages(kg + 64, n0, n1);
+      }
+      compute(buf_b, kg);
+      kg += 32;
+      if (!more) break;
+    }
   }
 
   // ---- merge the four waves ------------------------------------------------------
@@ -376,8 +450,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a,
   const int kvh = (gw / rows) % a.num_heads_kv;
   const int b = gw / (rows * a.num_heads_kv);
   const int seq = (int)a.seq_lens[b];
-  int lo;
-  key_range(a, seq, lo);
+  const int lo = key_origin(a, seq);
   const int n_splits = seq > lo ? (seq - lo + chunk - 1) / chunk : 0;
   const int qi = n / G, g = n - qi * G;
   const int head = kvh * G + g;
@@ -456,7 +529,9 @@ DecodePlan plan_decode(int32_t batch, int32_t q_len, int32_t num_heads_qo,
   const int64_t cap = (max_keys + 127) / 128 * 128;
   if (chunk > cap) chunk = std::max<int64_t>(cap, 128);
   p.chunk = (int32_t)chunk;
-  p.max_splits = max_keys > 0 ? (int32_t)((max_keys + chunk - 1) / chunk) : 1;
+  // range starts are rounded down to 32 keys: up to 31 extra keys
+  const int64_t span = window_left >= 0 ? max_keys + 31 : max_keys;
+  p.max_splits = span > 0 ? (int32_t)((span + chunk - 1) / chunk) : 1;
   p.workspace_bytes = p.max_splits > 1
                           ? (size_t)units * p.max_splits * p.rows * (kD + 2) * sizeof(float)
                           : 0;
