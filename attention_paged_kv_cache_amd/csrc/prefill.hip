@@ -38,6 +38,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "launch.h"
 #include "pkv_common.h"
 
@@ -193,60 +195,63 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   const int kv_clean = a.causal ? min(L_kv, shift + tok0 + 1) : L_kv;
   const int n_tiles = kv_end > 0 ? (kv_end + kKeys - 1) / kKeys : 0;
 
-  const int *bt = a.block_tables + (int64_t)b * a.max_pages;
+  const int32_t *__restrict__ bt = a.block_tables + (int64_t)b * a.max_pages;
   const int log2ps = __builtin_ctz(a.page_size);
   const int ps_mask = a.page_size - 1;
+  const int last_pg = L_kv > 0 ? (L_kv - 1) >> log2ps : 0;
+  const char *kbase = (const char *)a.k + (int64_t)kvh * a.head_stride_k * ES;
+  const char *vbase = (const char *)a.v + (int64_t)kvh * a.head_stride_v * ES;
+  const int64_t psk = a.page_stride_k * ES, psv = a.page_stride_v * ES;
+  const int64_t ssk = a.slot_stride_k * ES, ssv = a.slot_stride_v * ES;
 
   // Loader roles: waves 2..3 stage K, waves 0..1 stage V (transposed).
   const bool k_loader = wave >= 2;
   const int lt = tid & 127;
-  u32x4 stage[G_::NST];  // this thread's share of the next K or V tile
+  // One register array serves both roles (a wave is either a K or a V
+  // loader): K loaders keep their chunks of the next tile, V loaders 8 keys
+  // x 8 d (e4m3 in the low half of each entry).
+  u32x4 stage[G_::NST];
 
-  auto load_tile = [&](int j) {
-    const int kv0 = j * kKeys;
+  // Page ids of the (up to) four pages a 64-key tile spans. Indices are
+  // clamped into the sequence, so padding entries are never followed; keys
+  // past the end read the last page's tail and are masked (K) or zeroed (V).
+  auto tile_pages = [&](int j, int *p) {
+    const int pg0 = (j * kKeys) >> log2ps;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = bt[min(pg0 + i, last_pg)];
+  };
+  auto pick = [](const int *p, int idx) {
+    return idx == 0 ? p[0] : idx == 1 ? p[1] : idx == 2 ? p[2] : p[3];
+  };
+
+  // Issue the global loads of tile j (no waits: the data is consumed by
+  // store_tile one tile of compute later).
+  auto load_tile = [&](const int *p) {
     if (k_loader) {
-      const char *kb = (const char *)a.k + (int64_t)kvh * a.head_stride_k * ES;
 #pragma unroll
       for (int i = 0; i < G_::NKCH; ++i) {
         const int ch = lt + 128 * i;
         const int key = ch / G_::CPK, part = ch % G_::CPK;
-        const int gk = kv0 + key;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (gk < L_kv) {
-          const int page = bt[gk >> log2ps];
-          const int slot = gk & ps_mask;
-          v = ld16(kb + ((int64_t)page * a.page_stride_k +
-                         (int64_t)slot * a.slot_stride_k) * ES + part * 16);
-        }
-        stage[i] = v;
+        const int page = pick(p, key >> log2ps);
+        stage[i] = ld16(kbase + (int64_t)page * psk + (key & ps_mask) * ssk + part * 16);
       }
     } else {
       const int kg = lt & 7, dg = lt >> 3;
-      const char *vb = (const char *)a.v + (int64_t)kvh * a.head_stride_v * ES;
+      const int page = pick(p, (kg * 8) >> log2ps);
+      const char *vp = vbase + (int64_t)page * psv + ((kg * 8) & ps_mask) * ssv + dg * 8 * ES;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int gk = kv0 + kg * 8 + i;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (gk < L_kv) {
-          const int page = bt[gk >> log2ps];
-          const int slot = gk & ps_mask;
-          const char *p = vb + ((int64_t)page * a.page_stride_v +
-                                (int64_t)slot * a.slot_stride_v) * ES + dg * 8 * ES;
-          if (ES == 1) {
-            const u32x2 w = ld8(p);
-            const u32x2 lo = e4m3x4_to_bf16x4(w[0]);
-            const u32x2 hi = e4m3x4_to_bf16x4(w[1]);
-            v[0] = lo[0]; v[1] = lo[1]; v[2] = hi[0]; v[3] = hi[1];
-          } else {
-            v = ld16(p);
-          }
+        if constexpr (ES == 1) {
+          const u32x2 w = ld8(vp + i * ssv);
+          stage[i] = u32x4{w[0], w[1], 0u, 0u};
+        } else {
+          stage[i] = ld16(vp + i * ssv);
         }
-        stage[i] = v;
       }
     }
   };
 
-  auto store_tile = [&]() {
+  auto store_tile = [&](int j) {
     if (k_loader) {
 #pragma unroll
       for (int i = 0; i < G_::NKCH; ++i) {
@@ -256,8 +261,25 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
       }
     } else {
       const int kg = lt & 7, dg = lt >> 3;
-      u32x4 tr[8];
-      transpose8x8_b16(stage, tr);
+      u32x4 rows[8], tr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if constexpr (ES == 1) {
+          const u32x2 lo = e4m3x4_to_bf16x4(stage[i][0]);
+          const u32x2 hi = e4m3x4_to_bf16x4(stage[i][1]);
+          rows[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+          rows[i] = stage[i];
+        }
+      }
+      // keys past the sequence end: zero, so that p = 0 meets v = 0
+      const int kbeg = j * kKeys + kg * 8;
+      if (kbeg + 8 > L_kv) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (kbeg + i >= L_kv) rows[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+      transpose8x8_b16(rows, tr);
 #pragma unroll
       for (int cidx = 0; cidx < 8; ++cidx)
         st16(lds_vt + (dg * 8 + cidx) * kVtRow + kg * 16, tr[cidx]);
@@ -272,13 +294,21 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   float m_run = -INFINITY;
   float l_run = 0.0f;
 
-  if (n_tiles > 0) load_tile(0);
+  int pn[4];  // page ids of the next tile to load
+  if (n_tiles > 0) {
+    tile_pages(0, pn);
+    load_tile(pn);
+    if (n_tiles > 1) tile_pages(1, pn);
+  }
 
   for (int j = 0; j < n_tiles; ++j) {
     __syncthreads();
-    store_tile();
+    store_tile(j);
     __syncthreads();
-    if (j + 1 < n_tiles) load_tile(j + 1);
+    if (j + 1 < n_tiles) {
+      load_tile(pn);
+      if (j + 2 < n_tiles) tile_pages(j + 2, pn);
+    }
 
     // ---- S^T = K Q^T -------------------------------------------------------
     f32x16 sacc[2];
