@@ -125,9 +125,9 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   using G_ = Geo<ET, DQK>;
   using PT = typename PvTag<ET>::type;
   constexpr int ES = G_::ES;
+  // Two LDS stages: tile j is read from stage j % 2 while tile j + 1 is
+  // written into the other one.
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char *lds_k = smem;
-  char *lds_vt = smem + kKeys * G_::KROW;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -220,8 +220,10 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = bt[min(pg0 + i, last_pg)];
   };
-  auto pick = [](const int *p, int idx) {
-    return idx == 0 ? p[0] : idx == 1 ? p[1] : idx == 2 ? p[2] : p[3];
+  auto pick = [](const int *p, int idx) {  // p[idx] for idx in 0..3, branch-free
+    const int lo = (idx & 1) ? p[1] : p[0];
+    const int hi = (idx & 1) ? p[3] : p[2];
+    return (idx & 2) ? hi : lo;
   };
 
   // Issue the global loads of tile j (no waits: the data is consumed by
@@ -252,6 +254,8 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   };
 
   auto store_tile = [&](int j) {
+    char *lds_k = smem + (j & 1) * G_::LDS;
+    char *lds_vt = lds_k + kKeys * G_::KROW;
     if (k_loader) {
 #pragma unroll
       for (int i = 0; i < G_::NKCH; ++i) {
@@ -291,24 +295,29 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   for (int md = 0; md < 4; ++md)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[md][i] = 0.0f;
-  float m_run = -INFINITY;
+  // m_ref: the row's reference maximum (log2 units of the scaled score).
+  // It is raised lazily, only when a tile's maximum exceeds it by more than
+  // kLazy, so most tiles skip rescaling O; exponentials stay <= 2^kLazy.
+  constexpr float kLazy = 8.0f;
+  float m_ref = -INFINITY;
   float l_run = 0.0f;
 
   int pn[4];  // page ids of the next tile to load
   if (n_tiles > 0) {
     tile_pages(0, pn);
     load_tile(pn);
-    if (n_tiles > 1) tile_pages(1, pn);
+    store_tile(0);
+    if (n_tiles > 1) {
+      tile_pages(1, pn);
+      load_tile(pn);
+      if (n_tiles > 2) tile_pages(2, pn);
+    }
+    __syncthreads();
   }
 
   for (int j = 0; j < n_tiles; ++j) {
-    __syncthreads();
-    store_tile(j);
-    __syncthreads();
-    if (j + 1 < n_tiles) {
-      load_tile(pn);
-      if (j + 2 < n_tiles) tile_pages(j + 2, pn);
-    }
+    const char *lds_k = smem + (j & 1) * G_::LDS;
+    const char *lds_vt = lds_k + kKeys * G_::KROW;
 
     // ---- S^T = K Q^T -------------------------------------------------------
     f32x16 sacc[2];
@@ -346,10 +355,19 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
 #pragma unroll
       for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[mb][i]);
     mloc = wave_max_xor32(mloc);
-    const float m_new = fmaxf(m_run, mloc * c);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
+    const float m_tile = mloc * c;  // -inf when every key of the row is masked
+    const bool need = m_tile > m_ref + kLazy;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_new = need ? m_tile : m_ref;
+      const float alpha = need ? fast_exp2(m_ref - m_new) : 1.0f;
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < 4; ++md)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[md][i] *= alpha;
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
     float psum = 0.0f;
     u32x4 pb[4];  // P^T B operands, one per 16-key k-step
 #pragma unroll
@@ -363,11 +381,7 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
           psum += p0 + p1;
           pb[mb * 2 + hh][w2] = pack2(p0, p1, PT{});
         }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int md = 0; md < 4; ++md)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[md][i] *= alpha;
+    l_run += psum;
 
     // ---- O^T += V^T P^T --------------------------------------------------------
 #pragma unroll
@@ -379,6 +393,16 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
         o[md] = mfma_pv(av, pb[kstep], o[md], PT{});
       }
     }
+
+    // ---- stage tile j + 1 (its loads flew during this tile) -------------------
+    if (j + 1 < n_tiles) {
+      store_tile(j + 1);
+      if (j + 2 < n_tiles) {
+        load_tile(pn);
+        if (j + 3 < n_tiles) tile_pages(j + 3, pn);
+      }
+    }
+    __syncthreads();
   }
 
   // ---- epilogue ----------------------------------------------------------------
@@ -398,7 +422,7 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
       st8(op + d * 2, w);
     }
   if (half == 0)
-    a.lse[orow] = l_tot > 0.0f ? m_run * kLn2 + __logf(l_tot) : -INFINITY;
+    a.lse[orow] = l_tot > 0.0f ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
 }
 
 template <class ET, int DQK, class OT>
@@ -413,8 +437,16 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t s) {
       (int64_t)n_qtiles * a.batch * a.num_heads_kv * head_chunks;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  static bool lds_opt_in = false;  // two LDS stages exceed the 64 KB default
+  if (!lds_opt_in) {
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&prefill_kernel<ET, DQK, OT>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, 2 * G_::LDS);
+    if (e != hipSuccess) return e;
+    lds_opt_in = true;
+  }
   hipLaunchKernelGGL((prefill_kernel<ET, DQK, OT>), dim3((uint32_t)blocks),
-                     dim3(kThreads), G_::LDS, s, a, T, Gc, head_chunks,
+                     dim3(kThreads), 2 * G_::LDS, s, a, T, Gc, head_chunks,
                      n_qtiles);
   return hipGetLastError();
 }
