@@ -15,25 +15,30 @@
 //   qo head of the group. Each wave owns 32 rows.
 //
 // Per kv tile of 64 keys
-//   K:  gathered through the block table (16-byte loads per lane) into LDS
-//       as [key][d]; V: gathered 8 keys x 8 d per lane, transposed in
-//       registers, stored as V^T [d][key] so that the PV operand reads are
-//       16-byte runs along the key axis.
+//   K and V go from HBM straight into LDS with global_load_lds_dwordx4 (no
+//   staging registers): each wave gathers 16 keys of the tile, all in one
+//   page, through the block table. K rows are padded by 16 bytes so that the
+//   16 rows one read touches fall in distinct banks. V rows stay in the
+//   cache's [key][d] order with a 16-byte-chunk XOR swizzle, and the PV
+//   operand (V^T, keys along k) is read with the LDS transpose reads
+//   ds_read_b64_tr_b16 (ds_read_b64_tr_b8 for e4m3, widened after the read).
 //   S^T = K Q^T on 32x32 MFMA (A = K rows from LDS, B = Q from registers).
 //       In the S^T output a lane holds one query row and 32 of the tile's 64
 //       keys, so row max / sum are lane-local plus one exchange across the
 //       two half-waves.
 //   Online softmax in fp32 registers, exponent base 2 with log2(e) folded
-//       into the score scale.
+//       into the score scale; the row maximum used for the exponentials is
+//       raised lazily, so most tiles do not rescale O.
 //   O^T += V^T P^T on 32x32 MFMA (B = P^T straight from the S^T registers).
 //   The rows of the S^T MFMA are fed keys in the order pi(m) (bits 2 and 3
 //   of m swapped) so that a lane's 8 consecutive accumulator registers
 //   hold 8 consecutive keys: exactly the k-run of a PV B operand.
-//   Global loads of tile j+1 are issued before the MFMAs of tile j.
+//   Two LDS stages: tile j + 1 lands while tile j is computed; one barrier
+//   per tile.
 //
 // fp8 (e4m3fn) inputs: QK^T runs on the 32x32x64 f8f6f4 MFMA; V is widened
-// exactly to bf16 in the transpose, P is rounded to bf16, PV runs on bf16
-// MFMA. q_scale * k_scale folds into the score scale, v_scale into the
+// exactly to bf16 after the transpose read, P is rounded to bf16, PV runs on
+// bf16 MFMA. q_scale * k_scale folds into the score scale, v_scale into the
 // epilogue.
 
 #include <math.h>
@@ -51,7 +56,12 @@ constexpr int kThreads = 256;
 constexpr int kRows = 128;  // query rows per workgroup
 constexpr int kKeys = 64;   // keys per kv tile
 constexpr int kDvo = 128;   // value / output head dim
-constexpr int kVtRow = kKeys * 2 + 16;  // bytes per V^T row in LDS (padded)
+
+#define PKV_LDS __attribute__((address_space(3)))
+#define PKV_GLOBAL __attribute__((address_space(1)))
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 template <class ET>
 struct PvTag {  // 16-bit type of P and V^T for the PV MFMA
@@ -66,19 +76,29 @@ template <class ET, int DQK>
 struct Geo {
   static constexpr int ES = ET::bytes;
   static constexpr int ROWB = DQK * ES;                 // bytes of one K row
-  static constexpr int KROW = ROWB + 16;                // padded LDS row
-  static constexpr int CPK = ROWB / 16;                 // 16-B chunks per K row
-  static constexpr int NKCH = kKeys * CPK / 128;        // chunks per K loader
+  static constexpr int KRB = ROWB + 16;                 // padded K row in LDS
+  static constexpr int VRB = kDvo * ES;                 // V row (unpadded, swizzled)
   static constexpr int KB = (ES == 1) ? 32 : 16;        // k bytes per lane per MFMA
   static constexpr int KSTEPS = ROWB / (2 * KB);        // MFMA k-steps for QK^T
   static constexpr int NQ = ROWB / 32;                  // 16-B Q chunks per lane
-  static constexpr int LDS = kKeys * KROW + kDvo * kVtRow;
-  static constexpr int NST = NKCH > 8 ? NKCH : 8;       // staging registers
+  static constexpr int K_BYTES = kKeys * KRB;
+  static constexpr int V_BYTES = kKeys * VRB;
+  static constexpr int STAGE = K_BYTES + V_BYTES;       // one LDS stage
+  static constexpr int WK = 16 * KRB;                   // a wave's 16 K rows
+  static constexpr int K_INSTR = (WK + 1023) / 1024;    // 1 KB DMA writes per wave
+  static constexpr int V_INSTR = 16 * VRB / 1024;
 };
 
 // pi(m): swap bits 2 and 3 (an involution on 0..31).
 __device__ __forceinline__ int key_perm(int m) {
   return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// XOR applied to the 16-byte chunk index of V row `key` in LDS. It spreads
+// the rows one transpose read touches over distinct banks.
+template <int ES>
+__device__ __forceinline__ int vswz(int key) {
+  return ES == 2 ? 4 * (key & 3) : 2 * ((key >> 1) & 3);
 }
 
 __device__ __forceinline__ f32x16 mfma_qk(const u32x4 *a, const u32x4 *b,
@@ -118,6 +138,16 @@ __device__ __forceinline__ f32x16 mfma_pv(u32x4 a, u32x4 b, f32x16 c,
       __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// 16 bytes from global memory straight into LDS: lane l's bytes land at
+// lds_base + 16 * l (lds_base must be the same for every lane).
+__device__ __forceinline__ void dma16(const char *g, char *lds_base) {
+  __builtin_amdgcn_global_load_lds((PKV_GLOBAL void *)g, (PKV_LDS void *)lds_base, 16,
+                                   0, 0);
+}
+
+// Wait until this wave's outstanding global loads (LDS DMA included) are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <class ET, int DQK, class OT>
 __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void prefill_kernel(
     PrefillArgs a, int32_t T, int32_t Gc, int32_t head_chunks,
@@ -125,13 +155,16 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   using G_ = Geo<ET, DQK>;
   using PT = typename PvTag<ET>::type;
   constexpr int ES = G_::ES;
-  // Two LDS stages: tile j is read from stage j % 2 while tile j + 1 is
-  // written into the other one.
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  // Two LDS stages of [K rows | V rows]: tile j is read from one while tile
+  // j + 1 lands in the other. Two distinct arrays (not one buffer indexed by
+  // j % 2) let the compiler see that the DMA into one stage never aliases
+  // the reads of the other, so it does not wait for the DMA before them.
+  __shared__ __attribute__((aligned(16))) char lds_s0[G_::STAGE];
+  __shared__ __attribute__((aligned(16))) char lds_s1[G_::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -195,7 +228,10 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   const int kv_clean = a.causal ? min(L_kv, shift + tok0 + 1) : L_kv;
   const int n_tiles = kv_end > 0 ? (kv_end + kKeys - 1) / kKeys : 0;
 
-  const int32_t *__restrict__ bt = a.block_tables + (int64_t)b * a.max_pages;
+  // block table row through the constant address space: scalar loads
+  const __attribute__((address_space(4))) int32_t *bt =
+      (const __attribute__((address_space(4))) int32_t *)(a.block_tables) +
+      (int64_t)b * a.max_pages;
   const int log2ps = __builtin_ctz(a.page_size);
   const int ps_mask = a.page_size - 1;
   const int last_pg = L_kv > 0 ? (L_kv - 1) >> log2ps : 0;
@@ -204,91 +240,54 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   const int64_t psk = a.page_stride_k * ES, psv = a.page_stride_v * ES;
   const int64_t ssk = a.slot_stride_k * ES, ssv = a.slot_stride_v * ES;
 
-  // Loader roles: waves 2..3 stage K, waves 0..1 stage V (transposed).
-  const bool k_loader = wave >= 2;
-  const int lt = tid & 127;
-  // One register array serves both roles (a wave is either a K or a V
-  // loader): K loaders keep their chunks of the next tile, V loaders 8 keys
-  // x 8 d (e4m3 in the low half of each entry).
-  u32x4 stage[G_::NST];
+  // Each wave gathers keys r0 .. r0+15 of every tile; they share one page
+  // (page sizes 16, 32, 64). The page index is clamped into the sequence so
+  // that padding entries of the block table are never followed.
+  const int r0 = 16 * wave;
+  auto wave_page = [&](int j) { return bt[min((j * kKeys + r0) >> log2ps, last_pg)]; };
 
-  // Page ids of the (up to) four pages a 64-key tile spans. Indices are
-  // clamped into the sequence, so padding entries are never followed; keys
-  // past the end read the last page's tail and are masked (K) or zeroed (V).
-  auto tile_pages = [&](int j, int *p) {
-    const int pg0 = (j * kKeys) >> log2ps;
+  // Issue the LDS DMA of this wave's 16 K rows and 16 V rows of tile j.
+  // Keys past the sequence end are written as zeros instead.
+  auto issue_tile = [&](int j, int page, char *stage) {
+    const int key0 = j * kKeys + r0;
+    const int slot0 = key0 & ps_mask;
+    const char *kp = kbase + (int64_t)page * psk + (int64_t)slot0 * ssk;
+    const char *vp = vbase + (int64_t)page * psv + (int64_t)slot0 * ssv;
+    char *kl = stage + r0 * G_::KRB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = bt[min(pg0 + i, last_pg)];
-  };
-  auto pick = [](const int *p, int idx) {  // p[idx] for idx in 0..3, branch-free
-    const int lo = (idx & 1) ? p[1] : p[0];
-    const int hi = (idx & 1) ? p[3] : p[2];
-    return (idx & 2) ? hi : lo;
-  };
-
-  // Issue the global loads of tile j (no waits: the data is consumed by
-  // store_tile one tile of compute later).
-  auto load_tile = [&](const int *p) {
-    if (k_loader) {
-#pragma unroll
-      for (int i = 0; i < G_::NKCH; ++i) {
-        const int ch = lt + 128 * i;
-        const int key = ch / G_::CPK, part = ch % G_::CPK;
-        const int page = pick(p, key >> log2ps);
-        stage[i] = ld16(kbase + (int64_t)page * psk + (key & ps_mask) * ssk + part * 16);
+    for (int q = 0; q < G_::K_INSTR; ++q) {
+      const int byte = q * 1024 + lane * 16;
+      const int row = byte / G_::KRB;
+      const int col = byte - row * G_::KRB;
+      if (byte < G_::WK && col < G_::ROWB) {
+        if (key0 + row < L_kv) dma16(kp + row * ssk + col, kl + q * 1024);
+        else st16(kl + byte, u32x4{0u, 0u, 0u, 0u});
       }
-    } else {
-      const int kg = lt & 7, dg = lt >> 3;
-      const int page = pick(p, (kg * 8) >> log2ps);
-      const char *vp = vbase + (int64_t)page * psv + ((kg * 8) & ps_mask) * ssv + dg * 8 * ES;
+    }
+    char *vl = stage + G_::K_BYTES + r0 * G_::VRB;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if constexpr (ES == 1) {
-          const u32x2 w = ld8(vp + i * ssv);
-          stage[i] = u32x4{w[0], w[1], 0u, 0u};
-        } else {
-          stage[i] = ld16(vp + i * ssv);
-        }
-      }
+    for (int q = 0; q < G_::V_INSTR; ++q) {
+      const int byte = q * 1024 + lane * 16;
+      const int row = byte / G_::VRB;
+      const int pc = (byte - row * G_::VRB) >> 4;
+      const int lc = pc ^ vswz<ES>(row);
+      if (key0 + row < L_kv) dma16(vp + row * ssv + lc * 16, vl + q * 1024);
+      else st16(vl + byte, u32x4{0u, 0u, 0u, 0u});
     }
   };
 
-  auto store_tile = [&](int j) {
-    char *lds_k = smem + (j & 1) * G_::LDS;
-    char *lds_vt = lds_k + kKeys * G_::KROW;
-    if (k_loader) {
+  // Per-lane parts of the V^T transpose-read addresses (see vswz).
+  const int li = lane & 15, lg = (lane >> 4) & 1, lt4 = (li >> 2) & 3;
+  int v_lane, v_md[4];
+  if constexpr (ES == 2) {
+    v_lane = (8 * half + (li >> 2)) * G_::VRB + 32 * lg + 16 * ((li & 3) >> 1) + 8 * (li & 1);
 #pragma unroll
-      for (int i = 0; i < G_::NKCH; ++i) {
-        const int ch = lt + 128 * i;
-        const int key = ch / G_::CPK, part = ch % G_::CPK;
-        st16(lds_k + key * G_::KROW + part * 16, stage[i]);
-      }
-    } else {
-      const int kg = lt & 7, dg = lt >> 3;
-      u32x4 rows[8], tr[8];
+    for (int md = 0; md < 4; ++md) v_md[md] = 64 * (md ^ lt4);
+  } else {
+    v_lane = (8 * half + (li >> 1)) * G_::VRB + 16 * lg + 8 * (li & 1);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if constexpr (ES == 1) {
-          const u32x2 lo = e4m3x4_to_bf16x4(stage[i][0]);
-          const u32x2 hi = e4m3x4_to_bf16x4(stage[i][1]);
-          rows[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        } else {
-          rows[i] = stage[i];
-        }
-      }
-      // keys past the sequence end: zero, so that p = 0 meets v = 0
-      const int kbeg = j * kKeys + kg * 8;
-      if (kbeg + 8 > L_kv) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (kbeg + i >= L_kv) rows[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-      transpose8x8_b16(rows, tr);
-#pragma unroll
-      for (int cidx = 0; cidx < 8; ++cidx)
-        st16(lds_vt + (dg * 8 + cidx) * kVtRow + kg * 16, tr[cidx]);
-    }
-  };
+    for (int md = 0; md < 4; ++md) v_md[md] = 32 * (md ^ lt4);
+  }
 
   f32x16 o[4];
 #pragma unroll
@@ -302,22 +301,22 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   float m_ref = -INFINITY;
   float l_run = 0.0f;
 
-  int pn[4];  // page ids of the next tile to load
+  int pg_next = 0;
   if (n_tiles > 0) {
-    tile_pages(0, pn);
-    load_tile(pn);
-    store_tile(0);
-    if (n_tiles > 1) {
-      tile_pages(1, pn);
-      load_tile(pn);
-      if (n_tiles > 2) tile_pages(2, pn);
-    }
+    issue_tile(0, wave_page(0), lds_s0);
+    if (n_tiles > 1) pg_next = wave_page(1);
+    wait_vmem();
     __syncthreads();
   }
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const char *lds_k = smem + (j & 1) * G_::LDS;
-    const char *lds_vt = lds_k + kKeys * G_::KROW;
+  // One kv tile: compute from `cur` while tile j + 1 lands in `nxt`.
+  auto tile_step = [&](int j, const char *cur, char *nxt) {
+    const char *lds_k = cur;
+    const char *lds_v = cur + G_::K_BYTES;
+    if (j + 1 < n_tiles) {
+      issue_tile(j + 1, pg_next, nxt);
+      if (j + 2 < n_tiles) pg_next = wave_page(j + 2);
+    }
 
     // ---- S^T = K Q^T -------------------------------------------------------
     f32x16 sacc[2];
@@ -325,7 +324,7 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[mb][i] = 0.0f;
-      const char *krow = lds_k + (mb * 32 + key_perm(l32)) * G_::KROW;
+      const char *krow = lds_k + (mb * 32 + key_perm(l32)) * G_::KRB;
 #pragma unroll
       for (int s = 0; s < G_::KSTEPS; ++s) {
         u32x4 av[2];
@@ -383,26 +382,38 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
         }
     l_run += psum;
 
-    // ---- O^T += V^T P^T --------------------------------------------------------
+    // ---- O^T += V^T P^T (V^T through LDS transpose reads) -----------------
 #pragma unroll
     for (int kstep = 0; kstep < 4; ++kstep) {
 #pragma unroll
       for (int md = 0; md < 4; ++md) {
-        const u32x4 av =
-            ld16(lds_vt + (md * 32 + l32) * kVtRow + (kstep * 16 + half * 8) * 2);
+        const char *vptr = lds_v + kstep * 16 * G_::VRB + v_lane + v_md[md];
+        u32x4 av;
+        if constexpr (ES == 2) {
+          const i16x4 r0v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PKV_LDS i16x4 *)vptr);
+          const i16x4 r1v =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((PKV_LDS i16x4 *)(vptr + 4 * G_::VRB));
+          const u32x2 w0 = __builtin_bit_cast(u32x2, r0v), w1 = __builtin_bit_cast(u32x2, r1v);
+          av = u32x4{w0[0], w0[1], w1[0], w1[1]};
+        } else {
+          const i32x2 r8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PKV_LDS i32x2 *)vptr);
+          const u32x2 lo = e4m3x4_to_bf16x4((uint32_t)r8[0]);
+          const u32x2 hi = e4m3x4_to_bf16x4((uint32_t)r8[1]);
+          av = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
         o[md] = mfma_pv(av, pb[kstep], o[md], PT{});
       }
     }
 
-    // ---- stage tile j + 1 (its loads flew during this tile) -------------------
-    if (j + 1 < n_tiles) {
-      store_tile(j + 1);
-      if (j + 2 < n_tiles) {
-        load_tile(pn);
-        if (j + 3 < n_tiles) tile_pages(j + 3, pn);
-      }
-    }
+    // tile j + 1 has landed (this wave's DMA) and every wave is done with
+    // `cur` after this barrier
+    wait_vmem();
     __syncthreads();
+  };
+
+  for (int j = 0; j < n_tiles; j += 2) {
+    tile_step(j, lds_s0, lds_s1);
+    if (j + 1 < n_tiles) tile_step(j + 1, lds_s1, lds_s0);
   }
 
   // ---- epilogue ----------------------------------------------------------------
@@ -437,16 +448,8 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t s) {
       (int64_t)n_qtiles * a.batch * a.num_heads_kv * head_chunks;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  static bool lds_opt_in = false;  // two LDS stages exceed the 64 KB default
-  if (!lds_opt_in) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&prefill_kernel<ET, DQK, OT>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, 2 * G_::LDS);
-    if (e != hipSuccess) return e;
-    lds_opt_in = true;
-  }
   hipLaunchKernelGGL((prefill_kernel<ET, DQK, OT>), dim3((uint32_t)blocks),
-                     dim3(kThreads), 2 * G_::LDS, s, a, T, Gc, head_chunks,
+                     dim3(kThreads), 0, s, a, T, Gc, head_chunks,
                      n_qtiles);
   return hipGetLastError();
 }
