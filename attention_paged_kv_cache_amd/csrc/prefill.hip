@@ -56,6 +56,7 @@ constexpr int kThreads = 256;
 constexpr int kRows = 128;  // query rows per workgroup
 constexpr int kKeys = 64;   // keys per kv tile
 constexpr int kDvo = 128;   // value / output head dim
+constexpr int kXcds = 8;    // MI355X accelerator complex dies
 
 #define PKV_LDS __attribute__((address_space(3)))
 #define PKV_GLOBAL __attribute__((address_space(1)))
@@ -169,13 +170,20 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   const int l32 = lane & 31;
 
   // ---- which tile -------------------------------------------------------
-  const int bhc = a.batch * a.num_heads_kv * head_chunks;
-  const int bid = blockIdx.x;
-  const int qtile = n_qtiles - 1 - bid / bhc;
-  const int rem = bid % bhc;
-  const int b = rem / (a.num_heads_kv * head_chunks);
-  const int kvh = (rem / head_chunks) % a.num_heads_kv;
-  const int hc = rem % head_chunks;
+  // Workgroups are dispatched round-robin over the 8 XCDs (block i runs on
+  // XCD i % 8), each with its own L2. A "pair" (request, kv head, head
+  // chunk) owns one K/V stream; all query tiles of a pair are mapped to the
+  // same XCD and dispatched back to back, heaviest (last) tile first, so
+  // the pair's K/V pages are fetched from HBM once and re-read from L2.
+  const int n_pairs = a.batch * a.num_heads_kv * head_chunks;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot_in_xcd = blockIdx.x / kXcds;
+  const int pair = xcd + kXcds * (slot_in_xcd / n_qtiles);
+  if (pair >= n_pairs) return;
+  const int qtile = n_qtiles - 1 - slot_in_xcd % n_qtiles;
+  const int b = pair / (a.num_heads_kv * head_chunks);
+  const int kvh = (pair / head_chunks) % a.num_heads_kv;
+  const int hc = pair % head_chunks;
   const int L_q = a.lens_q[b];
   const int L_kv = a.lens_kv[b];
   const int tok0 = qtile * T;
@@ -319,20 +327,36 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
     }
 
     // ---- S^T = K Q^T -------------------------------------------------------
+    // The two 32-key m-blocks form two independent MFMA chains; their K
+    // fragment reads are issued a few steps ahead of the MFMAs that use them.
     f32x16 sacc[2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[mb][i] = 0.0f;
-      const char *krow = lds_k + (mb * 32 + key_perm(l32)) * G_::KRB;
+    {
+      const char *krow0 = lds_k + key_perm(l32) * G_::KRB;
 #pragma unroll
       for (int s = 0; s < G_::KSTEPS; ++s) {
-        u32x4 av[2];
 #pragma unroll
-        for (int u = 0; u < G_::KB / 16; ++u)
-          av[u] = ld16(krow + s * 2 * G_::KB + half * G_::KB + 16 * u);
-        sacc[mb] = mfma_qk(av, &qreg[s * (G_::KB / 16)], sacc[mb], ET{});
+        for (int mb = 0; mb < 2; ++mb) {
+          u32x4 av[2];
+#pragma unroll
+          for (int u = 0; u < G_::KB / 16; ++u)
+            av[u] = ld16(krow0 + mb * 32 * G_::KRB + s * 2 * G_::KB + half * G_::KB + 16 * u);
+          sacc[mb] = mfma_qk(av, &qreg[s * (G_::KB / 16)], sacc[mb], ET{});
+        }
       }
+      constexpr int kRd = G_::KB / 16;             // LDS reads per MFMA
+      constexpr int kMf = 2 * G_::KSTEPS;          // MFMAs
+      constexpr int kAhead = 2;                    // MFMAs of look-ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, kRd * kAhead, 0);
+#pragma unroll
+      for (int i = 0; i < kMf - kAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
     }
 
     // ---- mask (boundary tiles only) ----------------------------------------
@@ -367,24 +391,22 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
         for (int i = 0; i < 16; ++i) o[md][i] *= alpha;
     }
     const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
-    float psum = 0.0f;
-    u32x4 pb[4];  // P^T B operands, one per 16-key k-step
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          const float p0 = fast_exp2(fmaf(sacc[mb][hh * 8 + 2 * w2], c, -m_use));
-          const float p1 = fast_exp2(fmaf(sacc[mb][hh * 8 + 2 * w2 + 1], c, -m_use));
-          psum += p0 + p1;
-          pb[mb * 2 + hh][w2] = pack2(p0, p1, PT{});
-        }
-    l_run += psum;
 
-    // ---- O^T += V^T P^T (V^T through LDS transpose reads) -----------------
+    // ---- P and O^T += V^T P^T, one 16-key k-step at a time ------------------
+    // The exponentials of k-step k+1 run on the VALU while the MFMAs of
+    // k-step k execute. V^T comes from LDS transpose reads.
+    float psum = 0.0f;
 #pragma unroll
     for (int kstep = 0; kstep < 4; ++kstep) {
+      const int mb = kstep >> 1, hh = kstep & 1;
+      u32x4 pb;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const float p0 = fast_exp2(fmaf(sacc[mb][hh * 8 + 2 * w2], c, -m_use));
+        const float p1 = fast_exp2(fmaf(sacc[mb][hh * 8 + 2 * w2 + 1], c, -m_use));
+        psum += p0 + p1;
+        pb[w2] = pack2(p0, p1, PT{});
+      }
 #pragma unroll
       for (int md = 0; md < 4; ++md) {
         const char *vptr = lds_v + kstep * 16 * G_::VRB + v_lane + v_md[md];
@@ -401,9 +423,10 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
           const u32x2 hi = e4m3x4_to_bf16x4((uint32_t)r8[1]);
           av = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
-        o[md] = mfma_pv(av, pb[kstep], o[md], PT{});
+        o[md] = mfma_pv(av, pb, o[md], PT{});
       }
     }
+    l_run += psum;
 
     // tile j + 1 has landed (this wave's DMA) and every wave is done with
     // `cur` after this barrier
@@ -444,8 +467,8 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t s) {
   const int head_chunks = (G + Gc - 1) / Gc;
   const int T = kRows / Gc;
   const int n_qtiles = (a.max_q + T - 1) / T;
-  const int64_t blocks =
-      (int64_t)n_qtiles * a.batch * a.num_heads_kv * head_chunks;
+  const int64_t n_pairs = (int64_t)a.batch * a.num_heads_kv * head_chunks;
+  const int64_t blocks = (int64_t)kXcds * ((n_pairs + kXcds - 1) / kXcds) * n_qtiles;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((prefill_kernel<ET, DQK, OT>), dim3((uint32_t)blocks),
