@@ -99,11 +99,29 @@ __device__ __forceinline__ void transpose8x8_b16(const u32x4 in[8], u32x4 out[8]
   }
 }
 
+// Combine a value across the two 32-lane halves of a wave (lane l with lane
+// l ^ 32) with v_permlane32_swap, which swaps the high half of its first
+// operand with the low half of its second. Given two copies of x, the two
+// results hold x's low half twice and x's high half twice; no LDS traffic.
+// (The vector elements are copied to scalars before the bit casts: a bit
+// cast applied to a subscripted vector element has been seen to read
+// element 0.)
+__device__ __forceinline__ void halves_of(float x, float &lo, float &hi) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  lo = __builtin_bit_cast(float, r0);
+  hi = __builtin_bit_cast(float, r1);
+}
 __device__ __forceinline__ float wave_max_xor32(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+  float lo, hi;
+  halves_of(x, lo, hi);
+  return fmaxf(lo, hi);
 }
 __device__ __forceinline__ float wave_sum_xor32(float x) {
-  return x + __shfl_xor(x, 32);
+  float lo, hi;
+  halves_of(x, lo, hi);
+  return lo + hi;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) {
