@@ -38,10 +38,11 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["prefill", "decode", "spec", "fp8prefill", "append"],
-                   default=None, help="time one workload (for profiling runs)")
+    p.add_argument("--only", choices=["prefill", "decode", "spec", "fp8prefill", "copy"],
+                   default=None, help="time one workload (profiling runs); 'copy' times a "
+                                      "plain 1 GiB device copy used to calibrate HBM counters")
     return p.parse_args()
 
 
@@ -265,7 +266,13 @@ def main():
     import workloads
 
     if args.only:
-        if args.only in ("prefill", "fp8prefill"):
+        if args.only == "copy":
+            x = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
+            y = torch.empty_like(x)
+            ms, ms_l, ms_min = time_steps(lambda: y.copy_(x), args.steps, args.warmup)
+            r = {"GB/s": 2 * x.numel() * 4 / (ms_l * 1e-3) / 1e9, "bytes_read": x.numel() * 4,
+                 "bytes_written": x.numel() * 4, "ms_launch": ms_l}
+        elif args.only in ("prefill", "fp8prefill"):
             w, flops, ms, ms_l, ms_min = bench_prefill(pkv, torch, workloads, args.steps,
                                                        args.warmup, fp8=args.only == "fp8prefill")
             r = {"TFLOP/s": flops / (ms_l * 1e-3) / 1e12, "ms_launch": ms_l, "ms_min": ms_min}
@@ -286,7 +293,8 @@ def main():
                                                     args.warmup)
     tflops = flops / (ms * 1e-3) / 1e12
     tflops_launch = flops / (ms_launch * 1e-3) / 1e12
-    prefill_src = ("prefill.hip", "pkv_common.h")
+    prefill_src = ("prefill.hip", "pkv_common.h", "launch.h")
+    decode_src = ("decode.hip", "pkv_common.h", "launch.h")
 
     print("bench: fp8 prefill (d_qk 192)", file=sys.stderr, flush=True)
     w3, flops3, ms3, ms3_launch, _ = bench_prefill(pkv, torch, workloads, args.steps,
@@ -306,7 +314,6 @@ def main():
     del w5
     torch.cuda.empty_cache()
 
-    decode_src = ("decode.hip", "pkv_common.h")
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -337,7 +344,7 @@ def main():
             "value": round(flops3 / (ms3 * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
             "ms_per_step": round(ms3, 4),
             "roofline": roofline("mfma", flops3 / (ms3_launch * 1e-3) / 1e12, PEAK_FP8_TFLOPS,
-                                 "TFLOP/s", None),
+                                 "TFLOP/s", traffic("prefill_e4m3_d192", prefill_src)),
             "frac_of_bf16_peak": round(flops3 / (ms3_launch * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         },
         "decode": {
@@ -356,7 +363,7 @@ def main():
             "decode_value": round(bytes5 / (ms5_dec * 1e-3) / 1e9, 1), "unit": "GB/s",
             "decode_bytes": bytes5,
             "roofline": roofline("hbm", bytes5 / (ms5_dec * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s",
-                                 None),
+                                 traffic("spec_decode_e4m3", decode_src)),
             "append_ms": round(ms5_app, 4),
             "append_GBs": round(abytes5 / (ms5_app * 1e-3) / 1e9, 1),
         },
