@@ -519,10 +519,13 @@ DecodePlan plan_decode(int32_t batch, int32_t q_len, int32_t num_heads_qo,
                        : (int64_t)max_seq_len;
   const int64_t units = (int64_t)batch * num_heads_kv;
   // Enough workgroups to fill the chip, but chunks long enough that the
-  // partial (m, l, O) rows stay a small fraction of the K/V bytes.
+  // partial (m, l, O) rows, written once and read once by the merge, stay
+  // within 3% of the K/V bytes a chunk streams (at one byte per element;
+  // bf16 caches halve that share). With many query rows per kv head
+  // (drafts x GQA group) this leaves one chunk per request: no merge.
   int64_t c_bal = units > 0 ? (max_keys * units + 16383) / 16384 : max_keys;
-  const int64_t kv_bytes_per_key = 2 * (int64_t)head_dim;  // one byte per element at least
-  int64_t c_min = 20 * (int64_t)p.rows * (head_dim + 2) * 4 / kv_bytes_per_key;
+  const int64_t kv_bytes_per_key = 2 * (int64_t)head_dim;
+  int64_t c_min = 2 * (int64_t)p.rows * (head_dim + 2) * 4 * 100 / (3 * kv_bytes_per_key);
   int64_t chunk = std::max<int64_t>(c_bal, c_min);
   chunk = std::max<int64_t>(chunk, 128);
   chunk = (chunk + 127) / 128 * 128;

@@ -128,5 +128,7 @@ def test_workspace_sizes(lib):
     assert lib.pkv_prefill_workspace_size(16) >= 17 * 4
     # cfg-like decode sizes stay within the 128 MB the prefill page suggests
     assert 0 < lib.pkv_decode_workspace_size(256, 1, 32, 8, 128, 8192, -1) < 128 << 20
-    assert 0 < lib.pkv_decode_workspace_size(64, 4, 64, 8, 128, 32768, 4095) < 128 << 20
+    # many query rows per kv head: one chunk per request, no partials
+    assert lib.pkv_decode_workspace_size(64, 4, 64, 8, 128, 32768, 4095) == 0
+    assert 0 < lib.pkv_decode_workspace_size(64, 4, 64, 8, 128, 32768, -1) < 128 << 20
     assert lib.pkv_decode_workspace_size(4, 0, 32, 8, 128, 1024, -1) == 0

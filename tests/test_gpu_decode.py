@@ -67,6 +67,14 @@ def test_long_sequences_split_kv(pkv):
     check(pkv, small(batch=3, seq=(3000, 9000), seed=41))
 
 
+@pytest.mark.parametrize("window", [-1, 6000])
+def test_many_rows_split_kv_with_sinks(pkv, window):
+    # 32 query rows per kv head and sequences long enough for several splits:
+    # the merge combines partials and the sink term
+    check(pkv, small(batch=2, seq=(9000, 20000), q_len_per_req=4, num_qo_heads=16,
+                     num_kv_heads=2, window_left=window, sinks=True, seed=60))
+
+
 @pytest.mark.parametrize("ql,window,sinks", [(4, 100, True), (2, -1, True), (4, 0, False),
                                              (3, 37, False), (1, 5000, True)])
 def test_multi_query_window_sinks(pkv, ql, window, sinks):
