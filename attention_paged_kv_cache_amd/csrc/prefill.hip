@@ -15,10 +15,15 @@
 //   qo head of the group. Each wave owns 32 rows.
 //
 // Per kv tile of 64 keys
-//   K and V go from HBM straight into LDS with global_load_lds_dwordx4 (no
-//   staging registers): each wave gathers 16 keys of the tile, all in one
-//   page, through the block table. K rows are padded by 16 bytes so that the
-//   16 rows one read touches fall in distinct banks. V rows stay in the
+//   K and V go from HBM straight into LDS with buffer_load_dwordx4 ... lds
+//   (no staging registers): each wave gathers 16 keys of the tile, all in
+//   one page, through the block table, with a buffer resource bounded to
+//   that page. Every DMA instruction is a full one (keys past the sequence
+//   end reload the last key; their scores are masked), so the loads carry
+//   no branches and are spread between the MFMAs of the previous tile
+//   instead of arriving as one burst. K rows are padded by 16 bytes so that
+//   the 16 rows one read touches fall in distinct banks; each wave's 16 K
+//   rows occupy a whole number of KB. V rows stay in the
 //   cache's [key][d] order with a 16-byte-chunk XOR swizzle, and the PV
 //   operand (V^T, keys along k) is read with the LDS transpose reads
 //   ds_read_b64_tr_b16 (ds_read_b64_tr_b8 for e4m3, widened after the read).
@@ -59,7 +64,6 @@ constexpr int kDvo = 128;   // value / output head dim
 constexpr int kXcds = 8;    // MI355X accelerator complex dies
 
 #define PKV_LDS __attribute__((address_space(3)))
-#define PKV_GLOBAL __attribute__((address_space(1)))
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -82,11 +86,11 @@ struct Geo {
   static constexpr int KB = (ES == 1) ? 32 : 16;        // k bytes per lane per MFMA
   static constexpr int KSTEPS = ROWB / (2 * KB);        // MFMA k-steps for QK^T
   static constexpr int NQ = ROWB / 32;                  // 16-B Q chunks per lane
-  static constexpr int K_BYTES = kKeys * KRB;
+  static constexpr int WKB = (16 * KRB + 1023) / 1024 * 1024;  // a wave's K block
+  static constexpr int K_BYTES = 4 * WKB;
   static constexpr int V_BYTES = kKeys * VRB;
   static constexpr int STAGE = K_BYTES + V_BYTES;       // one LDS stage
-  static constexpr int WK = 16 * KRB;                   // a wave's 16 K rows
-  static constexpr int K_INSTR = (WK + 1023) / 1024;    // 1 KB DMA writes per wave
+  static constexpr int K_INSTR = WKB / 1024;            // 1 KB DMA writes per wave
   static constexpr int V_INSTR = 16 * VRB / 1024;
 };
 
@@ -139,11 +143,19 @@ __device__ __forceinline__ f32x16 mfma_pv(u32x4 a, u32x4 b, f32x16 c,
       __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// 16 bytes from global memory straight into LDS: lane l's bytes land at
-// lds_base + 16 * l (lds_base must be the same for every lane).
-__device__ __forceinline__ void dma16(const char *g, char *lds_base) {
-  __builtin_amdgcn_global_load_lds((PKV_GLOBAL void *)g, (PKV_LDS void *)lds_base, 16,
-                                   0, 0);
+// Buffer resource over `bytes` bytes from `base` (raw, untyped access).
+// Loads past the range return zeros instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, bytes, 0x00020000);
+}
+
+// 16 bytes at rsrc + voff straight into LDS: lane l's bytes land at
+// lds_base + 16 * l (lds_base must be the same for every lane). The buffer
+// form, unlike the flat global_load_lds, is not modelled by the compiler as
+// a flat access that may touch LDS, which would make every later LDS read
+// wait for all outstanding loads.
+__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, int voff, char *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (PKV_LDS void *)lds_base, 16, voff, 0, 0, 0);
 }
 
 // Wait until this wave's outstanding global loads (LDS DMA included) are done.
@@ -247,6 +259,8 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   const char *vbase = (const char *)a.v + (int64_t)kvh * a.head_stride_v * ES;
   const int64_t psk = a.page_stride_k * ES, psv = a.page_stride_v * ES;
   const int64_t ssk = a.slot_stride_k * ES, ssv = a.slot_stride_v * ES;
+  const int page_bytes_k = (int)((a.page_size - 1) * ssk + G_::ROWB);
+  const int page_bytes_v = (int)((a.page_size - 1) * ssv + G_::VRB);
 
   // Each wave gathers keys r0 .. r0+15 of every tile; they share one page
   // (page sizes 16, 32, 64). The page index is clamped into the sequence so
@@ -254,34 +268,62 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   const int r0 = 16 * wave;
   auto wave_page = [&](int j) { return bt[min((j * kKeys + r0) >> log2ps, last_pg)]; };
 
-  // Issue the LDS DMA of this wave's 16 K rows and 16 V rows of tile j.
-  // Keys past the sequence end are written as zeros instead.
-  auto issue_tile = [&](int j, int page, char *stage) {
+  // Per-lane source rows / columns of each 1 KB LDS DMA of this wave's 16 K
+  // rows (a whole number of KB per wave: lanes that fall in the row padding
+  // or past the 16th row load a valid duplicate into unused LDS bytes) and
+  // 16 V rows.
+  int k_row[G_::K_INSTR], k_col[G_::K_INSTR], v_row[G_::V_INSTR], v_col[G_::V_INSTR];
+#pragma unroll
+  for (int q = 0; q < G_::K_INSTR; ++q) {
+    const int byte = q * 1024 + lane * 16;
+    int row = byte / G_::KRB, col = byte - row * G_::KRB;
+    if (row > 15) { row = 15; col = 0; }
+    if (col >= G_::ROWB) col = G_::ROWB - 16;
+    k_row[q] = row;
+    k_col[q] = col;
+  }
+#pragma unroll
+  for (int q = 0; q < G_::V_INSTR; ++q) {
+    const int byte = q * 1024 + lane * 16;
+    const int row = byte / G_::VRB;
+    const int pc = (byte - row * G_::VRB) >> 4;
+    v_row[q] = row;
+    v_col[q] = (pc ^ vswz<ES>(row)) * 16;
+  }
+  // DMA state of the tile being loaded. Keys past the sequence end are
+  // loaded from the last key instead (finite data; their scores are masked,
+  // so their probabilities are exactly zero).
+  struct Dma {
+    __amdgpu_buffer_rsrc_t rk, rv;
+    int slot0, lim_row;
+    char *kl, *vl;
+  };
+  auto dma_prep = [&](int j, int page, char *stage) {
+    Dma d;
     const int key0 = j * kKeys + r0;
-    const int slot0 = key0 & ps_mask;
-    const char *kp = kbase + (int64_t)page * psk + (int64_t)slot0 * ssk;
-    const char *vp = vbase + (int64_t)page * psv + (int64_t)slot0 * ssv;
-    char *kl = stage + r0 * G_::KRB;
+    d.rk = make_rsrc(kbase + (int64_t)page * psk, page_bytes_k);
+    d.rv = make_rsrc(vbase + (int64_t)page * psv, page_bytes_v);
+    const bool in = key0 <= L_kv - 1;
+    d.slot0 = in ? (key0 & ps_mask) : ((L_kv - 1) & ps_mask);
+    d.lim_row = in ? (L_kv - 1 - key0) : 0;
+    d.kl = stage + wave * G_::WKB;
+    d.vl = stage + G_::K_BYTES + r0 * G_::VRB;
+    return d;
+  };
+  auto dma_k = [&](const Dma &d, int q) {
+    const int slot = d.slot0 + min(k_row[q], d.lim_row);
+    dma16b(d.rk, slot * (int)ssk + k_col[q], d.kl + q * 1024);
+  };
+  auto dma_v = [&](const Dma &d, int q) {
+    const int slot = d.slot0 + min(v_row[q], d.lim_row);
+    dma16b(d.rv, slot * (int)ssv + v_col[q], d.vl + q * 1024);
+  };
+  auto issue_tile = [&](int j, int page, char *stage) {
+    const Dma d = dma_prep(j, page, stage);
 #pragma unroll
-    for (int q = 0; q < G_::K_INSTR; ++q) {
-      const int byte = q * 1024 + lane * 16;
-      const int row = byte / G_::KRB;
-      const int col = byte - row * G_::KRB;
-      if (byte < G_::WK && col < G_::ROWB) {
-        if (key0 + row < L_kv) dma16(kp + row * ssk + col, kl + q * 1024);
-        else st16(kl + byte, u32x4{0u, 0u, 0u, 0u});
-      }
-    }
-    char *vl = stage + G_::K_BYTES + r0 * G_::VRB;
+    for (int q = 0; q < G_::K_INSTR; ++q) dma_k(d, q);
 #pragma unroll
-    for (int q = 0; q < G_::V_INSTR; ++q) {
-      const int byte = q * 1024 + lane * 16;
-      const int row = byte / G_::VRB;
-      const int pc = (byte - row * G_::VRB) >> 4;
-      const int lc = pc ^ vswz<ES>(row);
-      if (key0 + row < L_kv) dma16(vp + row * ssv + lc * 16, vl + q * 1024);
-      else st16(vl + byte, u32x4{0u, 0u, 0u, 0u});
-    }
+    for (int q = 0; q < G_::V_INSTR; ++q) dma_v(d, q);
   };
 
   // Per-lane parts of the V^T transpose-read addresses (see vswz).
@@ -312,7 +354,7 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   int pg_next = 0;
   if (n_tiles > 0) {
     issue_tile(0, wave_page(0), lds_s0);
-    if (n_tiles > 1) pg_next = wave_page(1);
+    pg_next = wave_page(1);
     wait_vmem();
     __syncthreads();
   }
@@ -321,10 +363,9 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   auto tile_step = [&](int j, const char *cur, char *nxt) {
     const char *lds_k = cur;
     const char *lds_v = cur + G_::K_BYTES;
-    if (j + 1 < n_tiles) {
-      issue_tile(j + 1, pg_next, nxt);
-      if (j + 2 < n_tiles) pg_next = wave_page(j + 2);
-    }
+    // Tile j + 1 (past the end: a harmless reload of the last key) is
+    // loaded into `nxt` by DMAs spread over this tile's MFMAs.
+    const Dma dn = dma_prep(j + 1, pg_next, nxt);
 
     // ---- S^T = K Q^T -------------------------------------------------------
     // The two 32-key m-blocks form two independent MFMA chains; their K
@@ -335,7 +376,8 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[mb][i] = 0.0f;
     {
-      const char *krow0 = lds_k + key_perm(l32) * G_::KRB;
+      const int kr = key_perm(l32);
+      const char *krow0 = lds_k + (kr >> 4) * G_::WKB + (kr & 15) * G_::KRB;
 #pragma unroll
       for (int s = 0; s < G_::KSTEPS; ++s) {
 #pragma unroll
@@ -343,10 +385,12 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
           u32x4 av[2];
 #pragma unroll
           for (int u = 0; u < G_::KB / 16; ++u)
-            av[u] = ld16(krow0 + mb * 32 * G_::KRB + s * 2 * G_::KB + half * G_::KB + 16 * u);
+            av[u] = ld16(krow0 + mb * 2 * G_::WKB + s * 2 * G_::KB + half * G_::KB + 16 * u);
           sacc[mb] = mfma_qk(av, &qreg[s * (G_::KB / 16)], sacc[mb], ET{});
         }
       }
+#pragma unroll
+      for (int q = 0; q < G_::K_INSTR; ++q) dma_k(dn, q);
       constexpr int kRd = G_::KB / 16;             // LDS reads per MFMA
       constexpr int kMf = 2 * G_::KSTEPS;          // MFMAs
       constexpr int kAhead = 2;                    // MFMAs of look-ahead
@@ -355,6 +399,7 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
       for (int i = 0; i < kMf - kAhead; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
+        if (i % 2 == 1 && i / 2 < G_::K_INSTR) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
     }
@@ -399,6 +444,11 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
 #pragma unroll
     for (int kstep = 0; kstep < 4; ++kstep) {
       const int mb = kstep >> 1, hh = kstep & 1;
+      if (kstep < G_::V_INSTR) dma_v(dn, kstep);
+      if (kstep == 3) {
+#pragma unroll
+        for (int q = 4; q < G_::V_INSTR; ++q) dma_v(dn, q);
+      }
       u32x4 pb;
 #pragma unroll
       for (int w2 = 0; w2 < 4; ++w2) {
@@ -427,6 +477,8 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
       }
     }
     l_run += psum;
+    // the page of tile j + 2 (read here, where its latency overlaps the wait)
+    pg_next = wave_page(j + 2);
 
     // tile j + 1 has landed (this wave's DMA) and every wave is done with
     // `cur` after this barrier
