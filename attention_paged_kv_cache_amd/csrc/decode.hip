@@ -94,9 +94,21 @@ __device__ __forceinline__ int key_origin(const DecodeArgs &a, int seq) {
 template <bool FP8>
 struct RawKV {
   using T = typename std::conditional<FP8, u32x2, u32x4>::type;
-  T k[2][4];  // [m-block][32-d k-step]
+  // K: 16-byte loads either way: 8 d of one k-step (16-bit) or 16 d of two
+  // k-steps (e4m3), [m-block][load]
+  u32x4 k[2][FP8 ? 2 : 4];
   T v[8];     // 8 keys x 8 d
 };
+
+// d offset of the 8 query elements lane group g4 feeds to k-step t. For
+// e4m3 K a lane loads 16 consecutive d (one 16-byte load) and feeds its two
+// halves to k-steps 2u and 2u + 1; Q uses the same assignment. Any
+// assignment that covers every d once per kv head gives the same dot
+// product.
+template <bool FP8>
+__device__ __forceinline__ int kstep_d(int t, int g4) {
+  return FP8 ? 64 * (t >> 1) + 16 * g4 + 8 * (t & 1) : 32 * t + 8 * g4;
+}
 
 // NB: number of 16-row blocks of the (q_len x G) query rows of a kv head.
 template <int NB, class QT, bool FP8>
@@ -151,7 +163,7 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok) v = ld16(qp + (s * 32 + g4 * 8) * 2);
+      if (ok) v = ld16(qp + kstep_d<FP8>(s, g4) * 2);
       v[0] ^= flip; v[1] ^= flip; v[2] ^= flip; v[3] ^= flip;
       qop[nb][s] = v;
     }
@@ -203,12 +215,10 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const int off = koff[mb];
-      const char *kp = ((off >> log2ps) ? kb1 : kb0) + ((kg0 + off) & ps_mask) * sstr + g4 * 8 * ES;
+      const char *kp = ((off >> log2ps) ? kb1 : kb0) + ((kg0 + off) & ps_mask) * sstr;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if constexpr (FP8) r.k[mb][s] = ld8(kp + s * 32 * ES);
-        else r.k[mb][s] = ld16(kp + s * 32 * ES);
-      }
+      for (int u = 0; u < (FP8 ? 2 : 4); ++u)
+        r.k[mb][u] = ld16(kp + kstep_d<FP8>(FP8 ? 2 * u : u, g4) * ES);
     }
     const char *vp = ((voff >> log2ps) ? vb1 : vb0) + ((kg0 + voff) & ps_mask) * sstr + r16 * 8 * ES;
 #pragma unroll
@@ -236,8 +246,12 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        if constexpr (FP8) kop[mb][s] = widen8(r.k[mb][s], QT{});
-        else kop[mb][s] = r.k[mb][s];
+        if constexpr (FP8) {
+          const u32x4 w = r.k[mb][s >> 1];
+          kop[mb][s] = widen8((s & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]}, QT{});
+        } else {
+          kop[mb][s] = r.k[mb][s];
+        }
       }
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
