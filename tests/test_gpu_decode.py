@@ -163,3 +163,34 @@ def test_full_size_append_then_spec_decode_sampled(pkv):
         page = int(w["block_tables"][b, p // ps])
         assert torch.equal(kv[page, 0, :, p % ps].view(torch.uint8),
                            w["k_append"][b * 4 + i].view(torch.uint8))
+
+
+@pytest.mark.parametrize("kv_dtype", [torch.bfloat16, torch.float8_e4m3fn])
+def test_poisoned_unused_memory_is_never_read(pkv, kv_dtype):
+    # NaN in every byte decode must not read: pool pages no request uses,
+    # tail slots past each sequence in its last page, and block-table padding
+    # pointing at a NaN page. The output must be bit-identical.
+    w = small(seed=47, batch=6, seq=(1, 900), q_len_per_req=3, window_left=150, sinks=True,
+              num_qo_heads=8, num_kv_heads=2, kv_dtype=kv_dtype)
+    kv = w["kv_cache"]
+    extra = 3
+    k8 = kv.view(torch.uint8)
+    pad = torch.zeros((extra,) + tuple(k8.shape[1:]), dtype=torch.uint8, device=DEV)
+    kv = torch.cat([k8, pad]).view(kv_dtype)
+    w = dict(w, kv_cache=kv)
+    out0 = run_decode(pkv, w)
+    nan = 0x7F if kv_dtype == torch.float8_e4m3fn else 0x7FC0
+    kvp = kv.clone()
+    raw = kvp.view(torch.uint8) if kv_dtype == torch.float8_e4m3fn else kvp.view(torch.int16)
+    n_pages = kv.shape[0] - extra
+    raw[n_pages:] = nan
+    ps = w["page_size"]
+    for b in range(w["block_tables"].shape[0]):
+        L = int(w["seq_lens"][b])
+        if L % ps:
+            p = int(w["block_tables"][b, L // ps])
+            raw[p, :, :, L % ps:] = nan  # HND: [page][K/V][head][slot][d]
+    bt = w["block_tables"].clone()
+    bt[bt < 0] = n_pages
+    out1 = run_decode(pkv, dict(w, kv_cache=kvp, block_tables=bt))
+    assert torch.equal(out0.view(torch.int16), out1.view(torch.int16))

@@ -1,0 +1,139 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a copy of ``oracle/attention.py`` (the text
+is edited in memory and loaded as a separate module; the oracle on disk is
+untouched) and checks that at least one independent pin rejects the
+mutant: torch's scaled-dot-product attention in float64 with a bottom-right
+mask built from tril / triu, a brute-force loop over the mask definition,
+or a closed form (sinks: o_sink = o * sigmoid(lse - sink); one allowed key:
+o = beta * v_j, lse = s_j).
+"""
+
+import os
+import types
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "attention.py")
+
+MUTATIONS = {
+    "top_left_causal": ("pos = t + (L_kv - L_q)", "pos = t"),
+    "strict_causal": ("ok &= j <= pos", "ok &= j < pos"),
+    "exclusive_window": ("ok &= j >= pos - window_left", "ok &= j > pos - window_left"),
+    "gqa_modulo_map": ("kh = h // G", "kh = h % H_kv"),
+    "dropped_score_scale": ("s = alpha * (q[:, h, :] @ k[:, kh, :].T)",
+                            "s = (q[:, h, :] @ k[:, kh, :].T)"),
+    "sink_dropped": ("z = p.sum(axis=1) + np.exp(sig - m)", "z = p.sum(axis=1)"),
+    "sink_in_numerator": ("o = (p @ v[:, kh, :]) / z[:, None]",
+                          "o = (p @ v[:, kh, :] + np.exp(sig - m)[:, None]) / z[:, None] "
+                          "if sinks is not None else (p @ v[:, kh, :]) / z[:, None]"),
+    "output_scale_dropped": ("beta * o, 0.0)", "o, 0.0)"),
+    "lse_base_2": ("m_s + np.log(np.where", "m_s + np.log2(np.where"),
+    "not_normalised": ("o = (p @ v[:, kh, :]) / z[:, None]", "o = (p @ v[:, kh, :])"),
+}
+
+
+def load_mutant(old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, old
+    mod = types.ModuleType("oracle._mutant")
+    mod.__package__ = "oracle"
+    mod.__file__ = SRC
+    exec(compile(text.replace(old, new), SRC, "exec"), mod.__dict__)
+    return mod
+
+
+# ---- independent pins ---------------------------------------------------------
+
+def br_mask(L_q, L_kv, w):
+    m = torch.ones(L_q, L_kv, dtype=torch.bool).tril(diagonal=L_kv - L_q)
+    if w >= 0:
+        m &= torch.ones(L_q, L_kv, dtype=torch.bool).triu(diagonal=L_kv - L_q - w)
+    return m
+
+
+def pin_sdpa(mod):
+    rng = np.random.default_rng(5)
+    for (L_q, L_kv, H_qo, H_kv, w) in [(3, 9, 4, 2, -1), (4, 13, 6, 3, 2), (2, 6, 4, 1, 0)]:
+        q = rng.standard_normal((L_q, H_qo, 16))
+        k = rng.standard_normal((L_kv, H_kv, 16))
+        v = rng.standard_normal((L_kv, H_kv, 8))
+        G = H_qo // H_kv
+        qt = torch.from_numpy(q).permute(1, 0, 2)
+        kt = torch.from_numpy(k).repeat_interleave(G, dim=1).permute(1, 0, 2)
+        vt = torch.from_numpy(v).repeat_interleave(G, dim=1).permute(1, 0, 2)
+        ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=br_mask(L_q, L_kv, w),
+                                             scale=0.37).permute(1, 0, 2).numpy() * 1.3
+        out, lse = mod.attention(q, k, v, 0.37, 1.3, True, window_left=w)
+        if not np.allclose(out, ref, rtol=1e-10, atol=1e-10):
+            return False
+        # natural-log LSE from logsumexp of the masked, scaled scores
+        s = 0.37 * torch.einsum("qhd,khd->hqk", qt.permute(1, 0, 2), kt.permute(1, 0, 2))
+        s = s.masked_fill(~br_mask(L_q, L_kv, w), float("-inf"))
+        if not np.allclose(lse, torch.logsumexp(s, dim=-1).T.numpy(), rtol=1e-10, atol=1e-10):
+            return False
+    return True
+
+
+def pin_brute_force_mask(mod):
+    for L_q in range(1, 5):
+        for L_kv in range(0, 7):
+            for w in (-1, 0, 1, 3):
+                got = mod.allowed_mask(np.arange(L_q), L_q, L_kv, True, w)
+                for t in range(L_q):
+                    pos = t + L_kv - L_q
+                    for j in range(L_kv):
+                        want = j <= pos and (w < 0 or j >= pos - w)
+                        if bool(got[t, j]) != want:
+                            return False
+    return True
+
+
+def pin_sinks_closed_form(mod):
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((3, 4, 16))
+    k = rng.standard_normal((10, 2, 16))
+    v = rng.standard_normal((10, 2, 8))
+    sinks = rng.standard_normal(4)
+    o0, lse = mod.attention(q, k, v, 0.5, 1.0, True)
+    o1, _ = mod.attention(q, k, v, 0.5, 1.0, True, sinks=sinks)
+    sig = 1.0 / (1.0 + np.exp(-(lse - sinks[None, :])))
+    return np.allclose(o1, o0 * sig[:, :, None], rtol=1e-10, atol=1e-12)
+
+
+def pin_one_key(mod):
+    # window_left = 0 with causal: each query sees only its own position
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((2, 2, 16))
+    k = rng.standard_normal((5, 1, 16))
+    v = rng.standard_normal((5, 1, 8))
+    out, lse = mod.attention(q, k, v, 0.25, 2.0, True, window_left=0)
+    for t in range(2):
+        j = t + 3
+        for h in range(2):
+            if not np.allclose(out[t, h], 2.0 * v[j, 0], rtol=1e-12, atol=1e-12):
+                return False
+            if not np.isclose(lse[t, h], 0.25 * q[t, h] @ k[j, 0], rtol=1e-12, atol=1e-12):
+                return False
+    return True
+
+
+PINS = [pin_sdpa, pin_brute_force_mask, pin_sinks_closed_form, pin_one_key]
+
+
+def test_pins_accept_the_oracle():
+    mod = load_mutant("import numpy as np", "import numpy as np")
+    for pin in PINS:
+        assert pin(mod), pin.__name__
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_reject_mutant(name):
+    mod = load_mutant(*MUTATIONS[name])
+    failed = [p.__name__ for p in PINS if not p(mod)]
+    assert failed, f"no pin caught the mutation {name}"
