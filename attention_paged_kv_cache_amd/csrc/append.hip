@@ -8,7 +8,8 @@
 // The append is a bit copy, bound by HBM bandwidth: every thread moves
 // 16-byte vectors, and a token's run of head_dim elements per head is
 // contiguous in both layouts (NHD and HND differ only in the head / slot
-// strides), so rows are copied as runs of 16-byte chunks.
+// strides), so rows are copied as runs of 16-byte chunks. K and V share
+// each row's page lookup.
 
 #include "launch.h"
 #include "pkv_common.h"
@@ -55,33 +56,50 @@ __global__ void csr_to_block_tables_kernel(const int32_t *__restrict__ indptr,
   bt[(int64_t)b * max_pages + k] = k < n ? indices[start + k] : -1;
 }
 
-// Flattened over (row, K|V, 16-byte chunk). chunks_per_row = heads *
-// row_bytes_per_head / 16. Consecutive threads take consecutive chunks of
-// one row, so both the read of the appended row and the write into the page
-// are 16-byte coalesced runs.
-__global__ __launch_bounds__(256) void append_kernel(AppendArgs a,
-                                                     int32_t chunks_per_head,
-                                                     int32_t chunks_per_row,
+// One thread per (row, pair of 16-byte chunks): it resolves the row's page
+// once (batch index -> position -> page id through kv_indptr/kv_indices,
+// and the slot) and moves the pair's bytes of both K and V, so four 16-byte
+// loads are in flight behind one lookup. Chunk c and c + half of a row go
+// to one thread, so consecutive threads read consecutive 16-byte pieces of
+// the appended rows and write consecutive pieces of each head's run. A
+// chunk is 16 bytes of one head's head_dim run, so a write never straddles
+// a head (or a page slot) in either layout.
+constexpr int kAppendChunks = 2;
+
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a, int32_t chunks_per_head,
+                                                     int32_t chunks_per_row, int32_t groups,
                                                      int64_t total) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= total) return;
-  const int32_t c = (int32_t)(gid % chunks_per_row);
-  const int64_t rk = gid / chunks_per_row;  // row * 2 + (0: K, 1: V)
-  const int32_t which = (int32_t)(rk & 1);
-  const int64_t row = rk >> 1;
+  const int32_t g = (int32_t)(gid % groups);
+  const int64_t row = gid / groups;
   const int32_t b = a.batch_indices[row];
   const int32_t p = a.positions[row];
   const int32_t page = a.kv_indices[a.kv_indptr[b] + p / a.page_size];
-  const int32_t slot = p % a.page_size;
-  const int32_t head = c / chunks_per_head;
-  const int32_t off = (c % chunks_per_head) * 16;
-  const char *src = (const char *)(which ? a.value : a.key) +
-                    row * (int64_t)chunks_per_row * 16 + (int64_t)c * 16;
-  char *dst = (char *)(which ? a.v_cache : a.k_cache) +
-              (int64_t)page * (which ? a.page_stride_v : a.page_stride_k) +
-              (int64_t)slot * a.slot_stride + (int64_t)head * a.head_stride +
-              off;
-  st16(dst, ld16(src));
+  const int64_t slot = (int64_t)(p % a.page_size) * a.slot_stride;
+  const char *ks = (const char *)a.key + row * chunks_per_row * 16;
+  const char *vs = (const char *)a.value + row * chunks_per_row * 16;
+  char *kd = (char *)a.k_cache + (int64_t)page * a.page_stride_k + slot;
+  char *vd = (char *)a.v_cache + (int64_t)page * a.page_stride_v + slot;
+  u32x4 kv[2][kAppendChunks];
+#pragma unroll
+  for (int u = 0; u < kAppendChunks; ++u) {
+    const int32_t c = g + u * groups;
+    if (c < chunks_per_row) {
+      kv[0][u] = ld16(ks + c * 16);
+      kv[1][u] = ld16(vs + c * 16);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kAppendChunks; ++u) {
+    const int32_t c = g + u * groups;
+    if (c < chunks_per_row) {
+      const int32_t head = c / chunks_per_head;
+      const int64_t o = (int64_t)head * a.head_stride + (c - head * chunks_per_head) * 16;
+      st16(kd + o, kv[0][u]);
+      st16(vd + o, kv[1][u]);
+    }
+  }
 }
 
 __global__ void exclusive_cumsum_kernel(const int32_t *__restrict__ lens,
@@ -142,10 +160,11 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
   if (a.nnz == 0) return hipSuccess;
   const int32_t chunks_per_head = a.row_bytes_per_head / 16;
   const int32_t chunks_per_row = chunks_per_head * a.num_heads;
-  const int64_t total = (int64_t)a.nnz * 2 * chunks_per_row;
+  const int32_t groups = (chunks_per_row + kAppendChunks - 1) / kAppendChunks;
+  const int64_t total = (int64_t)a.nnz * groups;
   const int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(append_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, a,
-                     chunks_per_head, chunks_per_row, total);
+                     chunks_per_head, chunks_per_row, groups, total);
   return hipGetLastError();
 }
 

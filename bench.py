@@ -8,8 +8,9 @@ U[0, 2048], 32 qo / 8 kv heads, head dim 128, HND pages of 16 tokens in a
 65536-page pool, bottom-right causal, fp32 LSE), reported as TFLOP/s of the
 unmasked (query, key) pairs. The same JSON line also carries decode (KV-read
 GB/s: batch 256, seq U[512, 8192], bf16) and append-then-speculative-decode
-(fp8 KV, window 4095, sinks, 4 drafts) measurements, each against the
-MI355X roofline, and the float64 oracle timed on the host for comparison.
+(fp8 KV, window 4095, sinks, 4 drafts) and bulk append (262144 fp8 rows)
+measurements, each against the MI355X roofline, and the float64 oracle timed
+on the host for comparison.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -40,7 +41,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["prefill", "decode", "spec", "fp8prefill", "copy"],
+    p.add_argument("--only", choices=["prefill", "decode", "spec", "fp8prefill", "append", "copy"],
                    default=None, help="time one workload (profiling runs); 'copy' times a "
                                       "plain 1 GiB device copy used to calibrate HBM counters")
     return p.parse_args()
@@ -212,6 +213,25 @@ def bench_spec(pkv, torch, workloads, steps, warmup):
     return w, nbytes, abytes, ms, ms_dec, ms_dec_min, ms_app
 
 
+def bench_bulk_append(pkv, torch, workloads, steps, warmup):
+    """Append 1024 rows into each of 256 requests (e4m3, 8 heads, d 128, HND
+    page 32): 512 MiB of K/V read and written per step."""
+    dev = "cuda:0"
+    w = workloads.bulk_append(dev)
+    nnz = w["k_append"].shape[0]
+    seq = w["seq_lens"].to(dev)
+    bi, pos = pkv.get_batch_indices_positions(w["append_indptr"].to(dev), seq, nnz)
+    idx, indptr, last = (w["kv_indices"].to(dev), w["kv_indptr"].to(dev),
+                         w["kv_last_page_len"].to(dev))
+
+    def step():
+        pkv.append_paged_kv_cache(w["k_append"], w["v_append"], bi, pos, w["kv_cache"], idx,
+                                  indptr, last, kv_layout=w["layout"])
+
+    ms, ms_launch, ms_min = time_steps(step, steps, warmup)
+    return w, append_bytes(nnz, w["num_kv_heads"], w["head_dim"], 1), ms, ms_launch, ms_min
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The float64 oracle on a bounded sample of the prefill workload: whole
     requests, in order, until about budget_s seconds of CPU work."""
@@ -276,6 +296,10 @@ def main():
             w, flops, ms, ms_l, ms_min = bench_prefill(pkv, torch, workloads, args.steps,
                                                        args.warmup, fp8=args.only == "fp8prefill")
             r = {"TFLOP/s": flops / (ms_l * 1e-3) / 1e12, "ms_launch": ms_l, "ms_min": ms_min}
+        elif args.only == "append":
+            w, nb, ms, ms_l, ms_min = bench_bulk_append(pkv, torch, workloads, args.steps,
+                                                        args.warmup)
+            r = {"GB/s": nb / (ms_l * 1e-3) / 1e9, "ms_launch": ms_l, "ms_min": ms_min}
         elif args.only == "decode":
             w, nb, ms, ms_l, ms_min = bench_decode(pkv, torch, workloads, args.steps, args.warmup)
             r = {"GB/s": nb / (ms_l * 1e-3) / 1e9, "ms_launch": ms_l, "ms_min": ms_min}
@@ -295,6 +319,7 @@ def main():
     tflops_launch = flops / (ms_launch * 1e-3) / 1e12
     prefill_src = ("prefill.hip", "pkv_common.h", "launch.h")
     decode_src = ("decode.hip", "pkv_common.h", "launch.h")
+    append_src = ("append.hip", "pkv_common.h", "launch.h")
 
     print("bench: fp8 prefill (d_qk 192)", file=sys.stderr, flush=True)
     w3, flops3, ms3, ms3_launch, _ = bench_prefill(pkv, torch, workloads, args.steps,
@@ -312,6 +337,12 @@ def main():
     w5, bytes5, abytes5, ms5, ms5_dec, ms5_dec_min, ms5_app = bench_spec(
         pkv, torch, workloads, args.steps, args.warmup)
     del w5
+    torch.cuda.empty_cache()
+
+    print("bench: bulk append (fp8 KV, 262144 rows)", file=sys.stderr, flush=True)
+    w6, bytes6, ms6, ms6_launch, _ = bench_bulk_append(pkv, torch, workloads, args.steps,
+                                                       args.warmup)
+    del w6
     torch.cuda.empty_cache()
 
     line = {
@@ -366,6 +397,14 @@ def main():
                                  traffic("spec_decode_e4m3", decode_src)),
             "append_ms": round(ms5_app, 4),
             "append_GBs": round(abytes5 / (ms5_app * 1e-3) / 1e9, 1),
+        },
+        "bulk_append": {
+            "workload": "append 1024 rows into each of 256 requests: e4m3 KV, 8 kv heads, d 128, "
+                        "HND page 32, seq U[4096,8192] after the append, pages in random order",
+            "value": round(bytes6 / (ms6 * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "ms_per_step": round(ms6, 4), "bytes_per_step": bytes6,
+            "roofline": roofline("hbm", bytes6 / (ms6_launch * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s",
+                                 traffic("append_bulk_e4m3", append_src)),
         },
     }
     if not args.no_cpu_baseline:

@@ -88,28 +88,35 @@ def test_append_example_bit_exact(pkv):
     assert not np.array_equal(got, before)
 
 
-@pytest.mark.parametrize("layout,dtype,ps,tuple_form", [
-    ("HND", torch.bfloat16, 16, False),
-    ("NHD", torch.float16, 32, True),
-    ("HND", torch.float8_e4m3fn, 32, False),
-    ("NHD", torch.float8_e4m3fn, 64, True),
+@pytest.mark.parametrize("layout,dtype,ps,tuple_form,B,H,D,seq_lo,seq_hi,app_hi", [
+    ("HND", torch.bfloat16, 16, False, 5, 3, 128, 1, 200, 40),
+    ("NHD", torch.float16, 32, True, 5, 3, 128, 1, 200, 40),
+    ("HND", torch.float8_e4m3fn, 32, False, 5, 3, 128, 1, 200, 40),
+    ("NHD", torch.float8_e4m3fn, 64, True, 5, 3, 128, 1, 200, 40),
+    # more than 8192 rows: several rows per wave, a ragged last wave
+    ("HND", torch.bfloat16, 16, False, 64, 2, 128, 200, 2000, 1000),
+    # 24-chunk heads (head_dim 192 e4m3), 36 chunks a row
+    ("HND", torch.float8_e4m3fn, 64, False, 40, 3, 192, 500, 1500, 1500),
+    # ~900k rows of 128 bytes: 64 rows per wave, several unrolled passes
+    ("NHD", torch.float16, 16, True, 400, 1, 64, 1500, 3000, 10 ** 6),
 ])
-def test_append_random_equals_oracle(pkv, layout, dtype, ps, tuple_form):
-    rng = np.random.default_rng(ps)
-    B, H, D = 5, 3, 128
-    seq = rng.integers(1, 200, size=B)
+def test_append_random_equals_oracle(pkv, layout, dtype, ps, tuple_form, B, H, D, seq_lo,
+                                     seq_hi, app_hi):
+    rng = np.random.default_rng(ps + B)
+    seq = rng.integers(seq_lo, seq_hi, size=B)
     npg = (seq + ps - 1) // ps
     pool = int(npg.sum()) + 7
     perm = rng.permutation(pool).astype(np.int32)
     indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
     indices = perm[: indptr[-1]]
     last = ((seq - 1) % ps + 1).astype(np.int32)
-    n_app = np.minimum(rng.integers(0, 40, size=B), seq)
+    n_app = np.minimum(rng.integers(0, app_hi, size=B), seq)
     ai = np.concatenate([[0], np.cumsum(n_app)]).astype(np.int32)
     nnz = int(ai[-1])
+    print(f"nnz {nnz}", flush=True)
     bi, pos = oracle.get_batch_indices_positions(ai, seq, nnz)
     page_shape = (ps, H, D) if layout == "NHD" else (H, ps, D)
-    gen = torch.Generator(device=DEV).manual_seed(ps)
+    gen = torch.Generator(device=DEV).manual_seed(ps + B)
     mk = lambda *s: torch.randn(*s, generator=gen, device=DEV).to(dtype)
     if tuple_form:
         cache = (mk(pool, *page_shape), mk(pool, *page_shape))
@@ -143,3 +150,44 @@ def test_append_empty_is_noop(pkv):
                               torch.tensor([1], dtype=torch.int32, device=DEV))
     torch.cuda.synchronize()
     assert int(cache.float().abs().sum()) == 0
+
+
+def test_bulk_append_full_size_sampled(pkv):
+    # the benchmark's bulk append (262144 e4m3 rows, HND page 32): every page
+    # of a sample of requests, touched slots and untouched ones, bit-exact
+    w = workloads.bulk_append(DEV)
+    kv = w["kv_cache"]
+    reqs = [0, 1, 77, 128, 255]
+    bt = w["block_tables"][reqs]
+    seq = w["seq_lens"][reqs]
+    ps = w["page_size"]
+    rows = int(w["append_indptr"][1])
+    n_pages = [(int(s) + ps - 1) // ps for s in seq]
+    before, bt_c = workloads.compact_pages(kv, bt, n_pages)
+    before = bits(before)
+    seq_d = w["seq_lens"].to(DEV)
+    nnz = w["k_append"].shape[0]
+    bi, pos = pkv.get_batch_indices_positions(w["append_indptr"].to(DEV), seq_d, nnz)
+    pkv.append_paged_kv_cache(w["k_append"], w["v_append"], bi, pos, kv,
+                              w["kv_indices"].to(DEV), w["kv_indptr"].to(DEV),
+                              w["kv_last_page_len"].to(DEV), kv_layout="HND")
+    torch.cuda.synchronize()
+    got, _ = workloads.compact_pages(kv, bt, n_pages)
+    got = bits(got)
+    indptr = np.concatenate([[0], np.cumsum(n_pages)]).astype(np.int32)
+    indices = np.concatenate([bt_c[i, :n_pages[i]].numpy() for i in range(len(reqs))])
+    last = ((seq.numpy() - 1) % ps + 1).astype(np.int32)
+    ai = np.arange(len(reqs) + 1, dtype=np.int32) * rows
+    bi_r, pos_r = oracle.get_batch_indices_positions(ai, seq.numpy(), rows * len(reqs))
+    src = np.concatenate([np.arange(b * rows, (b + 1) * rows) for b in reqs])
+    idx = torch.tensor(src, device=DEV)
+    ref = before.copy()
+    oracle.append_paged_kv_cache(bits(w["k_append"].index_select(0, idx)),
+                                 bits(w["v_append"].index_select(0, idx)), bi_r, pos_r,
+                                 ref[:, 0], ref[:, 1], indices, indptr, last, "HND")
+    assert np.array_equal(got, ref)
+    assert not np.array_equal(got, before)
+    # the device's batch indices and positions are the oracle's for the sample
+    bi_all, pos_all = bi.cpu().numpy(), pos.cpu().numpy()
+    assert np.array_equal(pos_all[src], pos_r)
+    assert np.array_equal(bi_all[src], np.repeat(reqs, rows))

@@ -180,6 +180,37 @@ def spec_decode(device="cpu", seed=5, batch=64, seq=(4096, 32768), num_qo_heads=
                 window_left=window_left, sinks=sinks, layout=HND)
 
 
+def bulk_append(device="cpu", seed=6, batch=256, seq=(4096, 8192), rows=1024,
+                num_kv_heads=8, head_dim=128, page_size=32,
+                kv_dtype=torch.float8_e4m3fn, layout=HND):
+    """A bandwidth-sized append (beyond the pages' examples, which are
+    launch-bound): ``rows`` new K/V rows per request (a chunk of prefill)
+    written at the end of each sequence (seq_lens ~ U{seq} are the lengths
+    after the append), into a cache of exactly the pages the requests own, in
+    random order, with the same layout as the speculative-decode workload.
+    At the defaults 512 MiB is read and 512 MiB written, well beyond the
+    chip's 256 MB last-level cache."""
+    host, dev = _gens(seed, device)
+    sl = _uniform_int(host, seq[0], seq[1], batch).to(torch.int64)
+    bt, pool = _page_tables(sl.tolist(), page_size, None, host)
+    n_pages = [(int(s) + page_size - 1) // page_size for s in sl]
+    kv_indptr = torch.zeros(batch + 1, dtype=torch.int32)
+    kv_indptr[1:] = torch.tensor(n_pages, dtype=torch.int32).cumsum(0)
+    kv_indices = torch.cat([bt[b, :n_pages[b]] for b in range(batch)])
+    last = ((sl - 1) % page_size + 1).to(torch.int32)
+    shape = (pool, 2, num_kv_heads, page_size, head_dim) if layout == HND \
+        else (pool, 2, page_size, num_kv_heads, head_dim)
+    kv = _randn(shape, dev, device, kv_dtype)
+    nnz = batch * rows
+    k_append = _randn((nnz, num_kv_heads, head_dim), dev, device, kv_dtype)
+    v_append = _randn((nnz, num_kv_heads, head_dim), dev, device, kv_dtype)
+    return dict(kv_cache=kv, k_append=k_append, v_append=v_append, seq_lens=sl.to(torch.int32),
+                append_indptr=(torch.arange(batch + 1, dtype=torch.int32) * rows),
+                kv_indptr=kv_indptr, kv_indices=kv_indices, kv_last_page_len=last,
+                block_tables=bt, page_size=page_size, num_kv_heads=num_kv_heads,
+                head_dim=head_dim, layout=layout)
+
+
 def compact_pages(cache, block_tables, n_pages_used, page_axis=0):
     """Host copy of just the pages a batch uses, and block tables renumbered
     into it (so an oracle need not hold a multi-GB pool). ``cache`` is any
