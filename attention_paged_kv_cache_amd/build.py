@@ -1,8 +1,10 @@
-"""Build libpkv.so (the HIP kernels and their C ABI) for gfx950 with hipcc.
+"""Build libpkv.so (the HIP kernels and their C ABI) for gfx950 with hipcc,
+and libpkv_ceiling.so (the chip-ceiling kernels the benchmark reads rates
+against; no part of the attention path).
 
 Run as ``python -m attention_paged_kv_cache_amd.build`` or through
 ``__graft_entry__.build()``. Objects go to ``_build/`` at the repository root;
-the shared library lands next to this file, where the binding loads it.
+the shared libraries land next to this file, where the binding loads them.
 """
 
 import os
@@ -16,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libpkv.so")
+CEILING_SRC = os.path.join(CSRC, "ceiling", "ceiling.hip")
+CEILING_OUT = os.path.join(PKG, "libpkv_ceiling.so")
 BUILD = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
@@ -60,21 +64,27 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False, jobs=None):
-    """Compile every .hip source and link libpkv.so. Always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 8)
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = OUT + ".tmp"
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose=False, jobs=None):
+    """Compile every .hip source and link libpkv.so and libpkv_ceiling.so.
+    Always rebuilds."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources() + [CEILING_SRC]
+    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 8)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:-1], OUT, verbose)
+    _link(objs[-1:], CEILING_OUT, verbose)
     return OUT
 
 

@@ -12,14 +12,24 @@ GB/s: batch 256, seq U[512, 8192], bf16) and append-then-speculative-decode
 measurements, each against the MI355X roofline, and the float64 oracle timed
 on the host for comparison.
 
+Rates come from warm back-to-back calls; each leg also reports the median of
+calls made after a 1 GiB write has evicted the caches ("flushed"). The
+measured ceilings (a pure MFMA loop, a streaming read, a copy) put the rates
+beside what this GPU reaches at all.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --only {prefill,fp8prefill,decode,spec,append,copy,ceilings,append_sweep}
 """
 
 import argparse
+import collections
+import ctypes
 import hashlib
 import json
 import math
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -41,9 +51,14 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["prefill", "decode", "spec", "fp8prefill", "append", "copy"],
+    p.add_argument("--no-flush", action="store_true",
+                   help="skip the cold-cache timings and the measured ceilings (kernel traces)")
+    p.add_argument("--only", choices=["prefill", "decode", "spec", "fp8prefill", "append", "copy",
+                                      "ceilings", "append_sweep"],
                    default=None, help="time one workload (profiling runs); 'copy' times a "
-                                      "plain 1 GiB device copy used to calibrate HBM counters")
+                                      "plain 1 GiB device copy used to calibrate HBM counters; "
+                                      "'append_sweep' times the append at 2^12..2^20 rows of "
+                                      "the append example's shape")
     return p.parse_args()
 
 
@@ -82,9 +97,18 @@ def append_bytes(nnz, h_kv, d, elem):
 
 # ---- timing -------------------------------------------------------------------
 
+Timing = collections.namedtuple("Timing", "region_ms launch_ms min_ms median_ms")
+
+
+def _stats(per, region_ms):
+    per = sorted(per)
+    return Timing(region_ms, sum(per) / len(per), per[0], statistics.median(per))
+
+
 def time_steps(fn, steps, warmup):
-    """(average ms per step over the whole region, average ms per launch from
-    events around each call). Events sit on the current stream, which is the
+    """Warm caches: `warmup` untimed calls, then `steps` calls back to back.
+    region_ms is the whole region per step; launch/min/median_ms come from
+    events around each call. Events sit on the current stream, which is the
     stream the library enqueues on."""
     import torch
     for _ in range(warmup):
@@ -101,8 +125,28 @@ def time_steps(fn, steps, warmup):
         b.record()
     end.record()
     torch.cuda.synchronize()
-    per = [a.elapsed_time(b) for a, b in ev]
-    return start.elapsed_time(end) / steps, sum(per) / len(per), min(per)
+    return _stats([a.elapsed_time(b) for a, b in ev], start.elapsed_time(end) / steps)
+
+
+def time_flushed(fn, steps, flush):
+    """Cold caches: before each timed call, write the whole of `flush` (a
+    1 GiB device buffer), which evicts the L2s and the 256 MB last-level
+    cache; only the call itself sits between its events. None when `flush`
+    is None."""
+    import torch
+    if flush is None:
+        return None
+    fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i, (a, b) in enumerate(ev):
+        flush.fill_(i & 0x7F)
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return _stats([a.elapsed_time(b) for a, b in ev], None)
 
 
 def kernel_hash(*files):
@@ -133,7 +177,8 @@ def roofline(bound, achieved, peak, unit, traffic_bytes):
 
 # ---- workloads -----------------------------------------------------------------
 
-def bench_prefill(pkv, torch, workloads, steps, warmup, fp8=False):
+def bench_prefill(pkv, torch, workloads, fp8=False):
+    """(workload, algorithmic FLOP, step)."""
     dev = "cuda:0"
     w = workloads.fp8_prefill(dev) if fp8 else workloads.batch_prefill(dev)
     lq, lkv = w["seq_lens_q"], w["seq_lens_kv"]
@@ -151,12 +196,12 @@ def bench_prefill(pkv, torch, workloads, steps, warmup, fp8=False):
             max_sequence_kv=mk, actual_seq_lens_q=lq_d, actual_seq_lens_kv=lkv_d,
             block_tables=bt_d, causal=True, out=out, lse=lse, kv_layout=w["layout"], **sc)
 
-    ms, ms_launch, ms_min = time_steps(step, steps, warmup)
     flops = prefill_flops(lq.tolist(), lkv.tolist(), w["num_qo_heads"], w["d_qk"], w["d_vo"])
-    return w, flops, ms, ms_launch, ms_min
+    return w, flops, step
 
 
-def bench_decode(pkv, torch, workloads, steps, warmup):
+def bench_decode(pkv, torch, workloads):
+    """(workload, algorithmic bytes, step)."""
     dev = "cuda:0"
     w = workloads.batch_decode(dev)
     ws = torch.zeros(max(pkv.decode_workspace_size(
@@ -169,13 +214,13 @@ def bench_decode(pkv, torch, workloads, steps, warmup):
                                        bmm1_scale=w["bmm1_scale"], bmm2_scale=1.0, out=out,
                                        kv_layout="HND")
 
-    ms, ms_launch, ms_min = time_steps(step, steps, warmup)
     nbytes = decode_bytes(w["seq_lens"].tolist(), 1, -1, 32, 8, 128, 2, 2, 2, 16)
-    return w, nbytes, ms, ms_launch, ms_min
+    return w, nbytes, step
 
 
-def bench_spec(pkv, torch, workloads, steps, warmup):
-    """Append 4 drafts per request, then decode them (one step = both)."""
+def bench_spec(pkv, torch, workloads):
+    """Append 4 drafts per request, then decode them (one step = both).
+    (workload, decode bytes, append bytes, append, decode)."""
     dev = "cuda:0"
     w = workloads.spec_decode(dev)
     B, ql = 64, 4
@@ -201,23 +246,14 @@ def bench_spec(pkv, torch, workloads, steps, warmup):
                                        window_left=w["window_left"], out=out, sinks=sinks,
                                        kv_layout="HND", q_len_per_req=ql)
 
-    def step():
-        append()
-        decode()
-
-    ms, _, _ = time_steps(step, steps, warmup)
-    _, ms_dec, ms_dec_min = time_steps(decode, steps, warmup)
-    _, ms_app, _ = time_steps(append, steps, warmup)
     nbytes = decode_bytes(w["seq_lens"].tolist(), ql, w["window_left"], 64, 8, 128, 1, 2, 2, 32)
     abytes = append_bytes(nnz, 8, 128, 1)
-    return w, nbytes, abytes, ms, ms_dec, ms_dec_min, ms_app
+    return w, nbytes, abytes, append, decode
 
 
-def bench_bulk_append(pkv, torch, workloads, steps, warmup):
-    """Append 1024 rows into each of 256 requests (e4m3, 8 heads, d 128, HND
-    page 32): 512 MiB of K/V read and written per step."""
+def bench_append(pkv, torch, w):
+    """(algorithmic bytes, step) for an append workload dict."""
     dev = "cuda:0"
-    w = workloads.bulk_append(dev)
     nnz = w["k_append"].shape[0]
     seq = w["seq_lens"].to(dev)
     bi, pos = pkv.get_batch_indices_positions(w["append_indptr"].to(dev), seq, nnz)
@@ -228,8 +264,63 @@ def bench_bulk_append(pkv, torch, workloads, steps, warmup):
         pkv.append_paged_kv_cache(w["k_append"], w["v_append"], bi, pos, w["kv_cache"], idx,
                                   indptr, last, kv_layout=w["layout"])
 
-    ms, ms_launch, ms_min = time_steps(step, steps, warmup)
-    return w, append_bytes(nnz, w["num_kv_heads"], w["head_dim"], 1), ms, ms_launch, ms_min
+    elem = w["k_append"].element_size()
+    return append_bytes(nnz, w["num_kv_heads"], w["head_dim"], elem), step
+
+
+# ---- measured ceilings -------------------------------------------------------------
+
+def measured_ceilings(torch, steps=10):
+    """Rates of a pure bf16 MFMA loop, a streaming 4 GiB read and a 1 GiB
+    device copy on this GPU (libpkv_ceiling.so), each the median of `steps`
+    timed calls after warm-up."""
+    path = os.path.join(ROOT, "attention_paged_kv_cache_amd", "libpkv_ceiling.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build first "
+                           "(python -m attention_paged_kv_cache_amd.build)")
+    lib = ctypes.CDLL(path)
+    lib.pkv_ceiling_mfma_bf16.restype = ctypes.c_int
+    lib.pkv_ceiling_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    lib.pkv_ceiling_mfma_bf16_flop.restype = ctypes.c_double
+    lib.pkv_ceiling_mfma_bf16_flop.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.pkv_ceiling_read.restype = ctypes.c_int
+    lib.pkv_ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    dev = "cuda:0"
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def ok(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} launch failed with hipError {rc}")
+
+    blocks, iters = 2048, 2000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    t = time_steps(lambda: ok(lib.pkv_ceiling_mfma_bf16(blocks, iters, out.data_ptr(), stream),
+                              "mfma loop"), steps, 3)
+    mfma = lib.pkv_ceiling_mfma_bf16_flop(blocks, iters) / (t.median_ms * 1e-3) / 1e12
+    del out
+
+    nbytes, rblocks = 4 << 30, 2048
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    words = torch.empty(rblocks * 256, dtype=torch.int32, device=dev)
+    t = time_steps(lambda: ok(lib.pkv_ceiling_read(buf.data_ptr(), nbytes, rblocks,
+                                                   words.data_ptr(), stream), "read stream"),
+                   steps, 3)
+    read = nbytes / (t.median_ms * 1e-3) / 1e9
+    del buf, words
+
+    x = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    y = torch.empty_like(x)
+    t = time_steps(lambda: y.copy_(x), steps, 3)
+    copy = 2 * x.numel() * 4 / (t.median_ms * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_loop_TFLOPs": round(mfma, 1), "hbm_read_4GiB_GBs": round(read, 1),
+            "hbm_copy_1GiB_GBs": round(copy, 1),
+            "what": "pure v_mfma_f32_32x32x16_bf16 loop (8 chains per wave, 8192 waves); "
+                    "streaming 16-byte loads over 4 GiB (2048 workgroups, one contiguous span each); torch copy_ of 1 GiB (read + write "
+                    "counted); medians of 10 calls"}
 
 
 def cpu_baseline(w, budget_s=12.0):
@@ -272,7 +363,23 @@ def cpu_baseline(w, budget_s=12.0):
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": f"first {n_req} of 16 requests of the prefill workload "
-                      f"({flops / 1e9:.1f} GFLOP algorithmic) in {dt:.1f} s, float64 numpy"}
+                      f"({flops / 1e9:.1f} GFLOP algorithmic) in {dt:.1f} s, float64 numpy "
+                      f"on {cpu_model()} ({os.cpu_count()} logical CPUs visible)"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown CPU"
+
+
+def rate(work, ms, scale):
+    return work / (ms * 1e-3) / scale
 
 
 def main():
@@ -286,73 +393,86 @@ def main():
     import workloads
 
     if args.only:
-        if args.only == "copy":
-            x = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
-            y = torch.empty_like(x)
-            ms, ms_l, ms_min = time_steps(lambda: y.copy_(x), args.steps, args.warmup)
-            r = {"GB/s": 2 * x.numel() * 4 / (ms_l * 1e-3) / 1e9, "bytes_read": x.numel() * 4,
-                 "bytes_written": x.numel() * 4, "ms_launch": ms_l}
-        elif args.only in ("prefill", "fp8prefill"):
-            w, flops, ms, ms_l, ms_min = bench_prefill(pkv, torch, workloads, args.steps,
-                                                       args.warmup, fp8=args.only == "fp8prefill")
-            r = {"TFLOP/s": flops / (ms_l * 1e-3) / 1e12, "ms_launch": ms_l, "ms_min": ms_min}
-        elif args.only == "append":
-            w, nb, ms, ms_l, ms_min = bench_bulk_append(pkv, torch, workloads, args.steps,
-                                                        args.warmup)
-            r = {"GB/s": nb / (ms_l * 1e-3) / 1e9, "ms_launch": ms_l, "ms_min": ms_min}
-        elif args.only == "decode":
-            w, nb, ms, ms_l, ms_min = bench_decode(pkv, torch, workloads, args.steps, args.warmup)
-            r = {"GB/s": nb / (ms_l * 1e-3) / 1e9, "ms_launch": ms_l, "ms_min": ms_min}
-        else:
-            w, nb, ab, ms, ms_d, ms_dmin, ms_a = bench_spec(pkv, torch, workloads, args.steps,
-                                                            args.warmup)
-            r = {"decode GB/s": nb / (ms_d * 1e-3) / 1e9, "ms_decode": ms_d,
-                 "ms_append": ms_a, "ms_step": ms}
-        print(json.dumps({"only": args.only, **{k: round(v, 4) for k, v in r.items()}}),
-              flush=True)
+        only(args, torch, pkv, workloads)
         return
 
-    print("bench: prefill (bf16, batch 16)", file=sys.stderr, flush=True)
-    w, flops, ms, ms_launch, ms_min = bench_prefill(pkv, torch, workloads, args.steps,
-                                                    args.warmup)
-    tflops = flops / (ms * 1e-3) / 1e12
-    tflops_launch = flops / (ms_launch * 1e-3) / 1e12
     prefill_src = ("prefill.hip", "pkv_common.h", "launch.h")
     decode_src = ("decode.hip", "pkv_common.h", "launch.h")
     append_src = ("append.hip", "pkv_common.h", "launch.h")
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    T, G = 1e12, 1e9
+
+    print("bench: prefill (bf16, batch 16)", file=sys.stderr, flush=True)
+    w, flops, step = bench_prefill(pkv, torch, workloads)
+    t1 = time_steps(step, args.steps, args.warmup)
+    f1 = time_flushed(step, args.steps, flush)
+    tokens, kv_tokens = int(w["seq_lens_q"].sum()), int(w["seq_lens_kv"].sum())
+    del w, step
+    torch.cuda.empty_cache()
 
     print("bench: fp8 prefill (d_qk 192)", file=sys.stderr, flush=True)
-    w3, flops3, ms3, ms3_launch, _ = bench_prefill(pkv, torch, workloads, args.steps,
-                                                   args.warmup, fp8=True)
-    del w3
+    w, flops3, step = bench_prefill(pkv, torch, workloads, fp8=True)
+    t3 = time_steps(step, args.steps, args.warmup)
+    f3 = time_flushed(step, args.steps, flush)
+    del w, step
     torch.cuda.empty_cache()
 
     print("bench: decode (bf16, batch 256)", file=sys.stderr, flush=True)
-    w4, bytes4, ms4, ms4_launch, ms4_min = bench_decode(pkv, torch, workloads, args.steps,
-                                                        args.warmup)
-    del w4
+    w, bytes4, step = bench_decode(pkv, torch, workloads)
+    t4 = time_steps(step, args.steps, args.warmup)
+    f4 = time_flushed(step, args.steps, flush)
+    del w, step
     torch.cuda.empty_cache()
 
     print("bench: append + speculative decode (fp8 KV)", file=sys.stderr, flush=True)
-    w5, bytes5, abytes5, ms5, ms5_dec, ms5_dec_min, ms5_app = bench_spec(
-        pkv, torch, workloads, args.steps, args.warmup)
-    del w5
+    w, bytes5, abytes5, append5, decode5 = bench_spec(pkv, torch, workloads)
+
+    def step5():
+        append5()
+        decode5()
+
+    t5 = time_steps(step5, args.steps, args.warmup)
+    t5d = time_steps(decode5, args.steps, args.warmup)
+    t5a = time_steps(append5, args.steps, args.warmup)
+    f5d = time_flushed(decode5, args.steps, flush)
+    del w, append5, decode5
     torch.cuda.empty_cache()
 
     print("bench: bulk append (fp8 KV, 262144 rows)", file=sys.stderr, flush=True)
-    w6, bytes6, ms6, ms6_launch, _ = bench_bulk_append(pkv, torch, workloads, args.steps,
-                                                       args.warmup)
-    del w6
+    w = workloads.bulk_append("cuda:0")
+    bytes6, step = bench_append(pkv, torch, w)
+    t6 = time_steps(step, args.steps, args.warmup)
+    f6 = time_flushed(step, args.steps, flush)
+    del w, step
+    flush = None
     torch.cuda.empty_cache()
 
+    ceil = None
+    if not args.no_flush:
+        print("bench: measured ceilings (MFMA loop, HBM read, copy)", file=sys.stderr,
+              flush=True)
+        ceil = measured_ceilings(torch)
+
+    def timing(t, f, work, scale):
+        d = {"ms_median": round(t.median_ms, 4), "ms_min": round(t.min_ms, 4)}
+        if f is not None:
+            d["flushed"] = {"ms_median": round(f.median_ms, 4),
+                            "value": round(rate(work, f.median_ms, scale), 1)}
+        return d
+
+    p_l = rate(flops, t1.launch_ms, T)
+    p3_l = rate(flops3, t3.launch_ms, T)
+    d4_l = rate(bytes4, t4.launch_ms, G)
+    d5_l = rate(bytes5, t5d.launch_ms, G)
+    a6_l = rate(bytes6, t6.launch_ms, G)
     line = {
         "metric": METRIC,
-        "value": round(tflops, 2),
+        "value": round(rate(flops, t1.region_ms, T), 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": round(t1.region_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -363,55 +483,119 @@ def main():
                         "kv_len = q_len + U[0,2048], 32 qo / 8 kv heads, d_qk = d_vo = 128, HND, "
                         "page 16, 65536-page pool in random order, bottom-right causal, fp32 LSE",
             "seed": 2,
-            "tokens": int(w["seq_lens_q"].sum()),
-            "kv_tokens": int(w["seq_lens_kv"].sum()),
+            "tokens": tokens,
+            "kv_tokens": kv_tokens,
             "flop_per_step": flops,
         },
-        "roofline": roofline("mfma", tflops_launch, PEAK_BF16_TFLOPS, "TFLOP/s",
+        "roofline": roofline("mfma", p_l, PEAK_BF16_TFLOPS, "TFLOP/s",
                              traffic("prefill_bf16", prefill_src)),
+        "timing": timing(t1, f1, flops, T),
         "fp8_prefill": {
             "workload": "e4m3 prefill, d_qk 192 / d_vo 128, batch 8, q_len = kv_len = 4096, "
                         "16/16 heads, page 64, per-tensor scales, causal, bf16 out",
-            "value": round(flops3 / (ms3 * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-            "ms_per_step": round(ms3, 4),
-            "roofline": roofline("mfma", flops3 / (ms3_launch * 1e-3) / 1e12, PEAK_FP8_TFLOPS,
-                                 "TFLOP/s", traffic("prefill_e4m3_d192", prefill_src)),
-            "frac_of_bf16_peak": round(flops3 / (ms3_launch * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "value": round(rate(flops3, t3.region_ms, T), 2), "unit": "TFLOP/s",
+            "ms_per_step": round(t3.region_ms, 4),
+            "roofline": roofline("mfma", p3_l, PEAK_FP8_TFLOPS, "TFLOP/s",
+                                 traffic("prefill_e4m3_d192", prefill_src)),
+            "frac_of_bf16_peak": round(p3_l / PEAK_BF16_TFLOPS, 4),
+            **timing(t3, f3, flops3, T),
         },
         "decode": {
             "workload": "decode over block_tables: bf16, batch 256, seq U[512,8192], 32/8 heads, "
                         "d 128, HND page 16, random pages, 1 query per request",
-            "value": round(bytes4 / (ms4 * 1e-3) / 1e9, 1), "unit": "GB/s",
-            "ms_per_step": round(ms4, 4), "bytes_per_step": bytes4,
-            "roofline": roofline("hbm", bytes4 / (ms4_launch * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s",
+            "value": round(rate(bytes4, t4.region_ms, G), 1), "unit": "GB/s",
+            "ms_per_step": round(t4.region_ms, 4), "bytes_per_step": bytes4,
+            "roofline": roofline("hbm", d4_l, PEAK_HBM_GBS, "GB/s",
                                  traffic("decode_bf16", decode_src)),
+            **timing(t4, f4, bytes4, G),
         },
         "spec_decode": {
             "workload": "append 4 drafts/request then decode: fp8 e4m3 KV, batch 64, "
                         "seq U[4096,32768], 64/8 heads, d 128, HND page 32, window_left 4095, "
                         "sinks, q_len_per_req 4",
-            "ms_per_step": round(ms5, 4),
-            "decode_value": round(bytes5 / (ms5_dec * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "ms_per_step": round(t5.region_ms, 4),
+            "decode_value": round(d5_l, 1), "unit": "GB/s",
             "decode_bytes": bytes5,
-            "roofline": roofline("hbm", bytes5 / (ms5_dec * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s",
+            "roofline": roofline("hbm", d5_l, PEAK_HBM_GBS, "GB/s",
                                  traffic("spec_decode_e4m3", decode_src)),
-            "append_ms": round(ms5_app, 4),
-            "append_GBs": round(abytes5 / (ms5_app * 1e-3) / 1e9, 1),
+            "decode": timing(t5d, f5d, bytes5, G),
+            "append_ms": round(t5a.launch_ms, 4),
+            "append_GBs": round(rate(abytes5, t5a.launch_ms, G), 1),
         },
         "bulk_append": {
             "workload": "append 1024 rows into each of 256 requests: e4m3 KV, 8 kv heads, d 128, "
                         "HND page 32, seq U[4096,8192] after the append, pages in random order",
-            "value": round(bytes6 / (ms6 * 1e-3) / 1e9, 1), "unit": "GB/s",
-            "ms_per_step": round(ms6, 4), "bytes_per_step": bytes6,
-            "roofline": roofline("hbm", bytes6 / (ms6_launch * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s",
+            "value": round(rate(bytes6, t6.region_ms, G), 1), "unit": "GB/s",
+            "ms_per_step": round(t6.region_ms, 4), "bytes_per_step": bytes6,
+            "roofline": roofline("hbm", a6_l, PEAK_HBM_GBS, "GB/s",
                                  traffic("append_bulk_e4m3", append_src)),
+            **timing(t6, f6, bytes6, G),
         },
     }
+    if ceil is not None:
+        line["measured_ceilings"] = {
+            **ceil,
+            "prefill_frac_of_mfma_loop": round(p_l / ceil["mfma_bf16_loop_TFLOPs"], 4),
+            "decode_frac_of_read": round(d4_l / ceil["hbm_read_4GiB_GBs"], 4),
+            "spec_decode_frac_of_read": round(d5_l / ceil["hbm_read_4GiB_GBs"], 4),
+            "bulk_append_frac_of_copy": round(a6_l / ceil["hbm_copy_1GiB_GBs"], 4),
+        }
     if not args.no_cpu_baseline:
         print("bench: float64 oracle on the host (bounded sample)", file=sys.stderr, flush=True)
-        w, *_ = bench_prefill(pkv, torch, workloads, 1, 0)
+        w, _, _ = bench_prefill(pkv, torch, workloads)
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
+
+
+def only(args, torch, pkv, workloads):
+    """One workload alone (profiling runs), or the append sweep, or the
+    ceilings; prints one JSON line per measurement."""
+    T, G = 1e12, 1e9
+    if args.only == "copy":
+        x = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        y = torch.empty_like(x)
+        t = time_steps(lambda: y.copy_(x), args.steps, args.warmup)
+        r = {"GB/s": rate(2 * x.numel() * 4, t.launch_ms, G), "bytes_read": x.numel() * 4,
+             "bytes_written": x.numel() * 4, "ms_launch": t.launch_ms}
+    elif args.only in ("prefill", "fp8prefill"):
+        w, flops, step = bench_prefill(pkv, torch, workloads, fp8=args.only == "fp8prefill")
+        t = time_steps(step, args.steps, args.warmup)
+        r = {"TFLOP/s": rate(flops, t.launch_ms, T), "ms_launch": t.launch_ms,
+             "ms_min": t.min_ms}
+    elif args.only == "append":
+        bytes6, step = bench_append(pkv, torch, workloads.bulk_append("cuda:0"))
+        t = time_steps(step, args.steps, args.warmup)
+        r = {"GB/s": rate(bytes6, t.launch_ms, G), "ms_launch": t.launch_ms, "ms_min": t.min_ms}
+    elif args.only == "decode":
+        w, nb, step = bench_decode(pkv, torch, workloads)
+        t = time_steps(step, args.steps, args.warmup)
+        r = {"GB/s": rate(nb, t.launch_ms, G), "ms_launch": t.launch_ms, "ms_min": t.min_ms}
+    elif args.only == "spec":
+        w, nb, ab, append, decode = bench_spec(pkv, torch, workloads)
+        td = time_steps(decode, args.steps, args.warmup)
+        ta = time_steps(append, args.steps, args.warmup)
+        r = {"decode GB/s": rate(nb, td.launch_ms, G), "ms_decode": td.launch_ms,
+             "ms_append": ta.launch_ms}
+    elif args.only == "ceilings":
+        r = measured_ceilings(torch)
+    else:  # append_sweep
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+        for k in range(12, 21):
+            w = workloads.append_sweep("cuda:0", nnz=1 << k)
+            nb, step = bench_append(pkv, torch, w)
+            t = time_steps(step, args.steps, args.warmup)
+            f = time_flushed(step, args.steps, flush)
+            print(json.dumps({"only": "append_sweep", "nnz": 1 << k, "bytes": nb,
+                              "GB/s": round(rate(nb, t.median_ms, G), 1),
+                              "flushed GB/s": round(rate(nb, f.median_ms, G), 1),
+                              "ms_median": round(t.median_ms, 4),
+                              "ms_flushed_median": round(f.median_ms, 4)}), flush=True)
+            del w, step
+            torch.cuda.empty_cache()
+        return
+    print(json.dumps({"only": args.only,
+                      **{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}}),
+          flush=True)
 
 
 if __name__ == "__main__":

@@ -211,6 +211,45 @@ def bulk_append(device="cpu", seed=6, batch=256, seq=(4096, 8192), rows=1024,
                 head_dim=head_dim, layout=layout)
 
 
+def append_sweep(device="cpu", nnz=4096, seed=1, num_kv_heads=32, head_dim=128, page_size=16,
+                 dtype=torch.float16):
+    """The append Example's shape family (fp16, 32 kv heads, d 128, NHD page
+    16) at ``nnz`` rows, for a bandwidth sweep: max(4, nnz / 1024) requests
+    each append their whole sequence (nnz split evenly, the remainder on the
+    last), into a pool of exactly the pages they own, in random order.
+    Values are filled in chunks so that no float32 copy of a large tensor is
+    ever held."""
+    host, dev = _gens(seed, device)
+    batch = max(4, nnz // 1024)
+    lens = torch.full((batch,), nnz // batch, dtype=torch.int64)
+    lens[-1] += nnz - int(lens.sum())
+    bt, pool = _page_tables(lens.tolist(), page_size, None, host)
+    n_pages = [(int(s) + page_size - 1) // page_size for s in lens]
+    kv_indptr = torch.zeros(batch + 1, dtype=torch.int32)
+    kv_indptr[1:] = torch.tensor(n_pages, dtype=torch.int32).cumsum(0)
+    kv_indices = torch.cat([bt[b, :n_pages[b]] for b in range(batch)])
+    last = ((lens - 1) % page_size + 1).to(torch.int32)
+
+    def filled(shape):
+        t = torch.empty(shape, dtype=dtype, device=device)
+        flat = t.view(-1)
+        step = 1 << 26
+        for i in range(0, flat.numel(), step):
+            n = min(step, flat.numel() - i)
+            flat[i:i + n] = torch.randn(n, generator=dev, device=device).to(dtype)
+        return t
+
+    kv = filled((pool, 2, page_size, num_kv_heads, head_dim))
+    k_append = filled((nnz, num_kv_heads, head_dim))
+    v_append = filled((nnz, num_kv_heads, head_dim))
+    ai = torch.zeros(batch + 1, dtype=torch.int32)
+    ai[1:] = lens.to(torch.int32).cumsum(0)
+    return dict(kv_cache=kv, k_append=k_append, v_append=v_append,
+                seq_lens=lens.to(torch.int32), append_indptr=ai, kv_indptr=kv_indptr,
+                kv_indices=kv_indices, kv_last_page_len=last, page_size=page_size,
+                num_kv_heads=num_kv_heads, head_dim=head_dim, layout=NHD)
+
+
 def compact_pages(cache, block_tables, n_pages_used, page_axis=0):
     """Host copy of just the pages a batch uses, and block tables renumbered
     into it (so an oracle need not hold a multi-GB pool). ``cache`` is any
