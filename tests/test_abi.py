@@ -132,3 +132,29 @@ def test_workspace_sizes(lib):
     assert lib.pkv_decode_workspace_size(64, 4, 64, 8, 128, 32768, 4095) == 0
     assert 0 < lib.pkv_decode_workspace_size(64, 4, 64, 8, 128, 32768, -1) < 128 << 20
     assert lib.pkv_decode_workspace_size(4, 0, 32, 8, 128, 1024, -1) == 0
+
+
+def test_ceiling_library_exports_and_validates():
+    # the chip-ceiling kernels the benchmark reads rates against
+    path = os.path.join(ROOT, "attention_paged_kv_cache_amd", "libpkv_ceiling.so")
+    if not os.path.exists(path):
+        pytest.fail("libpkv_ceiling.so is not built (run __graft_entry__.build())")
+    c = ctypes.CDLL(path)
+    c.pkv_ceiling_mfma_bf16_flop.restype = ctypes.c_double
+    c.pkv_ceiling_mfma_bf16_flop.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    # 2 blocks x 4 waves x 3 rounds x 8 chains x 32x32x16 MACs x 2
+    assert c.pkv_ceiling_mfma_bf16_flop(2, 3) == 2 * 4 * 3 * 8 * 32 * 32 * 16 * 2
+    c.pkv_ceiling_read.restype = ctypes.c_int
+    c.pkv_ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    c.pkv_ceiling_mfma_bf16.restype = ctypes.c_int
+    c.pkv_ceiling_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    # rejected on the host before any launch: a span that does not divide
+    # evenly, an unaligned buffer, null outputs, empty grids
+    dummy = ctypes.c_void_p(4096)
+    assert c.pkv_ceiling_read(dummy, 1000, 4, dummy, None) != 0
+    assert c.pkv_ceiling_read(ctypes.c_void_p(4100), 4 * 32768, 4, dummy, None) != 0
+    assert c.pkv_ceiling_read(dummy, 4 * 32768, 4, None, None) != 0
+    assert c.pkv_ceiling_mfma_bf16(0, 1, dummy, None) != 0
+    assert c.pkv_ceiling_mfma_bf16(1, 1, None, None) != 0
