@@ -21,7 +21,7 @@ than itself: the arrays the append page prints, closed forms, library routines
 (``torch.float8_e4m3fn``, ``scaled_dot_product_attention``) and brute force.
 """
 
-from .formats import decode_bits, e4m3fn_table, bits_dtype
+from .formats import decode_bits, e4m3fn_table, encode_e4m3fn, bits_dtype
 from .paging import (
     get_seq_lens,
     get_batch_indices_positions,

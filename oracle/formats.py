@@ -65,6 +65,34 @@ def e4m3fn_table():
 _E4M3_TABLE = e4m3fn_table()
 
 
+def encode_e4m3fn(x):
+    """float64 values (any shape) -> e4m3fn codes (uint8), from the format's
+    definition: the nearest finite e4m3fn value, a tie going to the code whose
+    mantissa is even; magnitudes above 448 saturate to +-448; NaN gives the
+    NaN code of its sign; -0.0 keeps its sign bit.
+
+    Decode page, Parameters: ``o_scale`` is the output scale for fp8 output.
+    The reading taken here mirrors how the per-tensor k/v scales dequantise
+    (value = scale * stored code), so a stored output code is
+    ``encode_e4m3fn(out / o_scale)``; saturating rather than producing NaN
+    on overflow is the reading for values beyond the format's range.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    mags = _E4M3_TABLE[:127]              # codes 0x00..0x7E: 0 .. 448, ascending
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.searchsorted(mags, a, side="left")   # first magnitude >= a
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - mags[lo]
+    d_hi = mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == mags[hi], hi, code)
+    sign = np.where(np.signbit(x), 0x80, 0x00)
+    out = (code | sign).astype(np.uint8)
+    return np.where(np.isnan(x), (sign | 0x7F).astype(np.uint8), out)
+
+
 def decode_bits(bits, fmt):
     """Raw bits (any shape) -> float64 values of format ``fmt``."""
     bits = np.asarray(bits)

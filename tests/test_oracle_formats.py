@@ -3,7 +3,7 @@
 import numpy as np
 import torch
 
-from oracle.formats import decode_bits, e4m3fn_table, F16, BF16, E4M3
+from oracle.formats import decode_bits, e4m3fn_table, encode_e4m3fn, F16, BF16, E4M3
 
 
 def test_e4m3fn_table_equals_torch_for_all_codes():
@@ -41,3 +41,41 @@ def test_decode_dispatch_keeps_shape():
     x = np.arange(24, dtype=np.uint8).reshape(2, 3, 4)
     assert decode_bits(x, E4M3).shape == (2, 3, 4)
     assert decode_bits(x.astype(np.uint16), BF16).shape == (2, 3, 4)
+
+
+def test_e4m3fn_encode_round_trips_every_finite_code():
+    tab = e4m3fn_table()
+    codes = np.arange(256)
+    fin = ~np.isnan(tab)
+    assert np.array_equal(encode_e4m3fn(tab[fin]), codes[fin].astype(np.uint8))
+
+
+def test_e4m3fn_encode_equals_torch_in_range():
+    # torch's float32 -> float8_e4m3fn conversion rounds to nearest even; on
+    # every float32 value with |x| <= 464 (where it has not overflowed to NaN)
+    # the two must agree: a dense sweep, every midpoint between neighbouring
+    # codes (the ties) and the float32 values on either side of each midpoint
+    mags = e4m3fn_table()[:127]
+    mid = ((mags[:-1] + mags[1:]) / 2).astype(np.float32)
+    below = np.nextafter(mid, np.float32(0))
+    above = np.nextafter(mid, np.float32(1e9))
+    xs = np.concatenate([np.linspace(-464, 464, 200001).astype(np.float32),
+                         mid, -mid, below, above, -below, -above])
+    ours = encode_e4m3fn(xs.astype(np.float64))
+    ref = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_e4m3fn_encode_ties_go_to_even_codes():
+    mags = e4m3fn_table()[:127]
+    mid = (mags[:-1] + mags[1:]) / 2
+    got = encode_e4m3fn(mid).astype(np.int64)
+    assert np.all(got % 2 == 0)
+    assert np.all((got == np.arange(126)) | (got == np.arange(1, 127)))
+
+
+def test_e4m3fn_encode_saturates_and_keeps_nan_and_signed_zero():
+    got = encode_e4m3fn([448.0, 449.0, 464.0, 1e30, np.inf, -1e30, -np.inf,
+                         np.nan, -np.nan, 0.0, -0.0, 2.0 ** -10, 2.0 ** -30])
+    assert got.tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE,
+                            0x7F, 0xFF, 0x00, 0x80, 0x00, 0x00]
