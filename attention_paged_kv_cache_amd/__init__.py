@@ -221,8 +221,13 @@ def decode_workspace_size(batch_size, q_len_per_req, num_heads_qo, num_heads_kv,
 def batch_decode_with_kv_cache(query, kv_cache, workspace_buffer, block_tables, seq_lens,
                                max_seq_len, bmm1_scale=1.0, bmm2_scale=1.0, window_left=-1,
                                out=None, out_dtype=None, sinks=None, kv_layout="HND",
-                               q_len_per_req=1):
-    """Batch decode over block_tables; returns out [num_tokens, num_heads, head_dim]."""
+                               q_len_per_req=1, o_scale=1.0):
+    """Batch decode over block_tables; returns out [num_tokens, num_heads, head_dim].
+
+    bmm1_scale / bmm2_scale are floats or one-element float32 device tensors
+    (read by the kernels at run time). With out_dtype torch.float8_e4m3fn each
+    stored code is e4m3fn(out / o_scale) (nearest, ties to even, saturating).
+    """
     layout = _layout(kv_layout)
     dev = query.device
     k, v, psk, psv = _split_cache(kv_cache)
@@ -255,12 +260,22 @@ def batch_decode_with_kv_cache(query, kv_cache, workspace_buffer, block_tables, 
         if sinks.numel() != h_qo:
             raise ValueError("sinks must hold one value per qo head")
         sink_ptr = sinks.data_ptr()
-    if isinstance(bmm1_scale, torch.Tensor) or isinstance(bmm2_scale, torch.Tensor):
-        raise ValueError("bmm1_scale / bmm2_scale must be Python floats here")
+    b1, b1_ptr = _scale_arg(bmm1_scale, dev, "bmm1_scale")
+    b2, b2_ptr = _scale_arg(bmm2_scale, dev, "bmm2_scale")
     _lib.check(_lib.load().pkv_batch_decode_with_kv_cache(
         _ptr(query), _ptr(k), _ptr(v), psk, psv, _ptr(workspace_buffer),
         workspace_buffer.numel() * workspace_buffer.element_size(), _ptr(bt), bt.shape[1],
-        _ptr(seq), batch, int(max_seq_len), float(bmm1_scale), float(bmm2_scale),
-        int(window_left), _ptr(out), _dt(out), sink_ptr, layout, int(q_len_per_req), h_qo,
-        hkv, d, ps, _dt(query), _dt(k), _stream()), "batch_decode_with_kv_cache")
+        _ptr(seq), batch, int(max_seq_len), b1, b2, int(window_left), _ptr(out), _dt(out),
+        sink_ptr, layout, int(q_len_per_req), h_qo, hkv, d, ps, _dt(query), _dt(k), b1_ptr,
+        b2_ptr, float(o_scale), None, 0, None, _stream()), "batch_decode_with_kv_cache")
     return out
+
+
+def _scale_arg(x, dev, name):
+    """(host float, device pointer or None) for a float or a one-element
+    float32 device tensor."""
+    if isinstance(x, torch.Tensor):
+        if x.dtype != torch.float32 or x.numel() != 1 or x.device != dev:
+            raise ValueError(f"{name} tensor must be one float32 element on {dev}")
+        return 1.0, x.data_ptr()
+    return float(x), None

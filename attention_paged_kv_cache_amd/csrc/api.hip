@@ -284,9 +284,14 @@ PKV_API pkv_status pkv_batch_decode_with_kv_cache(
     int32_t window_left, void *out, pkv_dtype out_dtype, const float *sinks,
     pkv_layout kv_layout, int32_t q_len_per_req, int32_t num_heads_qo,
     int32_t num_heads_kv, int32_t head_dim, int32_t page_size,
-    pkv_dtype q_dtype, pkv_dtype kv_dtype, void *stream) {
+    pkv_dtype q_dtype, pkv_dtype kv_dtype, const float *bmm1_scale_dev,
+    const float *bmm2_scale_dev, float o_scale, const int32_t *cum_seq_lens_q,
+    int32_t max_q_len, const uint8_t *spec_mask, void *stream) {
   CHECK(batch_size >= 0, PKV_ERR_INVALID_ARG, "batch_size < 0");
   CHECK(q_len_per_req >= 1, PKV_ERR_INVALID_ARG, "q_len_per_req < 1");
+  CHECK(cum_seq_lens_q == nullptr && max_q_len == 0 && spec_mask == nullptr,
+        PKV_ERR_UNSUPPORTED,
+        "variable-length queries and the speculative-decoding mask are not supported");
   CHECK(window_left >= -1, PKV_ERR_INVALID_ARG, "window_left < -1");
   CHECK(num_heads_kv > 0 && num_heads_qo > 0, PKV_ERR_INVALID_ARG,
         "head counts must be positive");
@@ -304,8 +309,10 @@ PKV_API pkv_status pkv_batch_decode_with_kv_cache(
         "query dtype must be F16 or BF16");
   CHECK(kv_dtype == q_dtype || kv_dtype == PKV_E4M3, PKV_ERR_UNSUPPORTED,
         "kv dtype must equal the query dtype or be E4M3");
-  CHECK(out_dtype == PKV_F16 || out_dtype == PKV_BF16, PKV_ERR_UNSUPPORTED,
-        "output dtype must be F16 or BF16");
+  CHECK(out_dtype == PKV_F16 || out_dtype == PKV_BF16 || out_dtype == PKV_E4M3,
+        PKV_ERR_UNSUPPORTED, "output dtype must be F16, BF16 or E4M3");
+  CHECK(out_dtype != PKV_E4M3 || (o_scale > 0.0f && o_scale <= 3.4e38f),
+        PKV_ERR_INVALID_ARG, "o_scale must be finite and > 0");
   CHECK(page_size_ok(page_size), PKV_ERR_UNSUPPORTED,
         "page_size must be 16, 32 or 64");
   CHECK(max_seq_len >= 0, PKV_ERR_INVALID_ARG, "max_seq_len < 0");
@@ -351,6 +358,9 @@ PKV_API pkv_status pkv_batch_decode_with_kv_cache(
   a.batch = batch_size;
   a.max_seq_len = max_seq_len;
   a.bmm1_scale = bmm1_scale;
+  a.bmm1_ptr = bmm1_scale_dev;
+  a.bmm2_ptr = bmm2_scale_dev;
+  a.o_scale = out_dtype == PKV_E4M3 ? o_scale : 1.0f;
   a.bmm2_scale = bmm2_scale;
   a.window_left = window_left;
   a.out = out;

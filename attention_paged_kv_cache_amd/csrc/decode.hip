@@ -143,7 +143,8 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
 
   const int G = a.num_heads_qo / a.num_heads_kv;
   const int rows = a.q_len * G;
-  const float c_raw = a.bmm1_scale * kLog2e;
+  const float bmm1 = a.bmm1_ptr ? a.bmm1_ptr[0] : a.bmm1_scale;
+  const float c_raw = bmm1 * kLog2e;
   const bool negate = c_raw < 0.0f;
   const float c = fmaxf(fabsf(c_raw), 1e-30f);
 
@@ -425,17 +426,27 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
       const int head = kvh * G + g;
       float den = L;
       if (a.sinks) den += fast_exp2(a.sinks[head] * kLog2e - M_use);
-      const float scale = den > 0.0f ? a.bmm2_scale / den : 0.0f;
-      char *op = (char *)a.out + ((int64_t)(b * a.q_len + qi) * a.num_heads_qo + head) * kD * 2;
-      u32x2 w;
-      if (a.out_dtype == 0) {
-        w[0] = pack2(src[0] * scale, src[1] * scale, F16Tag{});
-        w[1] = pack2(src[2] * scale, src[3] * scale, F16Tag{});
+      const float bmm2 = a.bmm2_ptr ? a.bmm2_ptr[0] : a.bmm2_scale;
+      const int64_t orow = (int64_t)(b * a.q_len + qi) * a.num_heads_qo + head;
+      if (a.out_dtype == 2) {
+        const float scale = den > 0.0f ? bmm2 / (den * a.o_scale) : 0.0f;
+        const uint32_t w = e4m3_encode(src[0] * scale) | (e4m3_encode(src[1] * scale) << 8) |
+                           (e4m3_encode(src[2] * scale) << 16) |
+                           (e4m3_encode(src[3] * scale) << 24);
+        *reinterpret_cast<uint32_t *>((char *)a.out + orow * kD + d4) = w;
       } else {
-        w[0] = pack2(src[0] * scale, src[1] * scale, BF16Tag{});
-        w[1] = pack2(src[2] * scale, src[3] * scale, BF16Tag{});
+        const float scale = den > 0.0f ? bmm2 / den : 0.0f;
+        char *op = (char *)a.out + orow * kD * 2;
+        u32x2 w;
+        if (a.out_dtype == 0) {
+          w[0] = pack2(src[0] * scale, src[1] * scale, F16Tag{});
+          w[1] = pack2(src[2] * scale, src[3] * scale, F16Tag{});
+        } else {
+          w[0] = pack2(src[0] * scale, src[1] * scale, BF16Tag{});
+          w[1] = pack2(src[2] * scale, src[3] * scale, BF16Tag{});
+        }
+        st8(op + d4 * 2, w);
       }
-      st8(op + d4 * 2, w);
     } else {
       const int64_t unit = ((int64_t)b * a.num_heads_kv + kvh) * max_splits + split;
       float *dst = ws_o + (unit * rows + n) * kD + d4;
@@ -468,7 +479,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a,
   const int n_splits = seq > lo ? (seq - lo + chunk - 1) / chunk : 0;
   const int qi = n / G, g = n - qi * G;
   const int head = kvh * G + g;
-  char *op = (char *)a.out + ((int64_t)(b * a.q_len + qi) * a.num_heads_qo + head) * kD * 2;
+  const int64_t orow = (int64_t)(b * a.q_len + qi) * a.num_heads_qo + head;
   if (n_splits == 1) return;  // written by the split kernel
   const int64_t unit0 = ((int64_t)b * a.num_heads_kv + kvh) * max_splits;
   float M = -INFINITY;
@@ -486,10 +497,17 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a,
     o1 += f * v[1];
   }
   if (a.sinks) L += fast_exp2(sink - M_use);
-  const float scale = L > 0.0f ? a.bmm2_scale / L : 0.0f;
+  const float bmm2 = a.bmm2_ptr ? a.bmm2_ptr[0] : a.bmm2_scale;
+  if (a.out_dtype == 2) {
+    const float scale = L > 0.0f ? bmm2 / (L * a.o_scale) : 0.0f;
+    const uint32_t w = e4m3_encode(o0 * scale) | (e4m3_encode(o1 * scale) << 8);
+    *reinterpret_cast<uint16_t *>((char *)a.out + orow * kD + lane * 2) = (uint16_t)w;
+    return;
+  }
+  const float scale = L > 0.0f ? bmm2 / L : 0.0f;
   uint32_t w = (a.out_dtype == 0) ? pack2(o0 * scale, o1 * scale, F16Tag{})
                                   : pack2(o0 * scale, o1 * scale, BF16Tag{});
-  *reinterpret_cast<uint32_t *>(op + lane * 4) = w;
+  *reinterpret_cast<uint32_t *>((char *)a.out + orow * kD * 2 + lane * 4) = w;
 }
 
 template <int NB, class QT, bool FP8>

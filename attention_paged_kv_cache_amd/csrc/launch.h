@@ -68,6 +68,8 @@ struct DecodeArgs {
   const uint32_t *seq_lens;
   int32_t batch, max_seq_len;
   float bmm1_scale, bmm2_scale;
+  const float *bmm1_ptr, *bmm2_ptr;  // device scalars replacing the floats, or null
+  float o_scale;                     // e4m3 output: stored code = e4m3(out / o_scale)
   int32_t window_left;
   void *out;
   const float *sinks;

@@ -62,6 +62,30 @@ __device__ __forceinline__ uint32_t pack2(float a, float b, F16Tag) {
          ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
+// fp32 -> e4m3fn code (low 8 bits): nearest value, ties to the even
+// mantissa; magnitudes above 448 saturate to +-448 (the format has no
+// infinity); NaN gives the NaN code of its sign. Written out in integer
+// arithmetic so the rounding is exactly this rule.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a != a) return sign | 0x7Fu;
+  if (a > 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) {  // below 2^-6: subnormal codes m * 2^-9, m = 0..8
+    return sign | (uint32_t)rintf(a * 512.0f);  // exact scaling, rint is RNE
+  }
+  int e = (int)((u >> 23) & 0xFFu) - 127;  // -6 .. 8
+  uint32_t keep = (u >> 20) & 0x7u;        // top 3 mantissa bits
+  const uint32_t rest = u & 0xFFFFFu;      // the 20 bits rounded away
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ++keep;
+  if (keep == 8u) {
+    keep = 0u;
+    ++e;
+  }
+  return sign | ((uint32_t)(e + 7) << 3) | keep;
+}
+
 // Four e4m3fn codes (one dword) -> four bf16 (two dwords). Exact: every
 // e4m3fn value is representable in bf16.
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 typedef enum {
   PKV_OK = 0,
@@ -199,11 +199,20 @@ size_t pkv_decode_workspace_size(int32_t batch_size, int32_t q_len_per_req,
  *   query [batch_size * q_len_per_req, num_heads_qo, head_dim], q_dtype BF16
  *         or F16
  *   out   [batch_size * q_len_per_req, num_heads_qo, head_dim], out_dtype
- *         BF16 or F16
+ *         BF16, F16 or E4M3. For E4M3 (the page's fp8 output with o_scale)
+ *         each stored code is e4m3fn(out / o_scale): nearest value, ties to
+ *         the even code, saturating at +-448, NaN kept; o_scale must be
+ *         finite and > 0 (it is ignored for the other output types).
  *   kv_dtype BF16, F16 or E4M3 (E4M3 values are used as stored: fold a
  *         per-tensor k scale into bmm1_scale and a v scale into bmm2_scale)
+ *   bmm1_scale_dev / bmm2_scale_dev  device float32 scalars or NULL; when
+ *         given they replace bmm1_scale / bmm2_scale (the page's tensor form
+ *         of the two scales), read by the kernels at run time
  *   seq_lens [batch_size] uint32; max_seq_len >= every entry
  *   sinks    [num_heads_qo] float32 logits or NULL
+ *   cum_seq_lens_q, max_q_len, spec_mask  variable-length queries and the
+ *         speculative-decoding mask (decode page, Parameters); must be NULL,
+ *         0 and NULL in this version (PKV_ERR_UNSUPPORTED otherwise)
  *   workspace >= pkv_decode_workspace_size(...) bytes (contents ignored)
  * Supported: head_dim == 128, num_heads_qo % num_heads_kv == 0,
  * q_len_per_req * num_heads_qo / num_heads_kv <= 64, page_size in
@@ -218,7 +227,9 @@ pkv_status pkv_batch_decode_with_kv_cache(
     int32_t window_left, void *out, pkv_dtype out_dtype, const float *sinks,
     pkv_layout kv_layout, int32_t q_len_per_req, int32_t num_heads_qo,
     int32_t num_heads_kv, int32_t head_dim, int32_t page_size,
-    pkv_dtype q_dtype, pkv_dtype kv_dtype, void *stream);
+    pkv_dtype q_dtype, pkv_dtype kv_dtype, const float *bmm1_scale_dev,
+    const float *bmm2_scale_dev, float o_scale, const int32_t *cum_seq_lens_q,
+    int32_t max_q_len, const uint8_t *spec_mask, void *stream);
 
 #ifdef __cplusplus
 }

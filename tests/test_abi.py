@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pkv_abi_version() == 1
+    assert lib.pkv_abi_version() == 2
 
 
 def _err(lib):
@@ -81,7 +81,8 @@ def _decode(lib, **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, psk=2 * 16 * 8 * 128, psv=2 * 16 * 8 * 128, ws=FAKE,
              ws_bytes=1 << 30, bt=FAKE, max_pages=64, seq=FAKE, batch=4, max_seq=1024,
              bmm1=0.1, bmm2=1.0, window=-1, out=FAKE, odt=1, sinks=None, layout=1, ql=1,
-             hqo=32, hkv=8, d=128, ps=16, qdt=1, kvdt=1, stream=None)
+             hqo=32, hkv=8, d=128, ps=16, qdt=1, kvdt=1, bmm1_dev=None, bmm2_dev=None,
+             o_scale=1.0, cum_q=None, max_q=0, mask=None, stream=None)
     a.update(over)
     return lib.pkv_batch_decode_with_kv_cache(*a.values())
 
@@ -97,6 +98,13 @@ def _decode(lib, **over):
     (dict(layout=3), "NHD or HND"),
     (dict(max_pages=1), "too narrow"),
     (dict(hqo=8, hkv=16), ">= num_heads_kv"),
+    (dict(odt=2, o_scale=0.0), "o_scale"),
+    (dict(odt=2, o_scale=-1.0), "o_scale"),
+    (dict(odt=2, o_scale=float("inf")), "o_scale"),
+    (dict(odt=2, o_scale=float("nan")), "o_scale"),
+    (dict(odt=7), "output dtype"),
+    (dict(cum_q=FAKE), "variable-length"),
+    (dict(mask=FAKE), "variable-length"),
 ])
 def test_decode_validation(lib, over, needle):
     st = _decode(lib, **over)

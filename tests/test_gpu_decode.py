@@ -194,3 +194,113 @@ def test_poisoned_unused_memory_is_never_read(pkv, kv_dtype):
     bt[bt < 0] = n_pages
     out1 = run_decode(pkv, dict(w, kv_cache=kvp, block_tables=bt))
     assert torch.equal(out0.view(torch.int16), out1.view(torch.int16))
+
+
+# ---- fp8 output with o_scale, device-tensor scales ---------------------------
+
+def _bf16_exact(vals):
+    """float64 values -> the bf16 values torch rounds them to (as float64)."""
+    return torch.tensor(vals, dtype=torch.float64).to(torch.bfloat16).double().numpy()
+
+
+def _encode_cases():
+    tab = oracle.e4m3fn_table()
+    mags = tab[:127]
+    mid = (mags[:-1] + mags[1:]) / 2
+    # the bf16 neighbours of each midpoint: one bf16 ulp either side
+    bits16 = torch.tensor(mid, dtype=torch.bfloat16).view(torch.int16)
+    below = (bits16 - 1).view(torch.bfloat16).double().numpy()
+    above = (bits16 + 1).view(torch.bfloat16).double().numpy()
+    extra = [448.0, 450.0, 464.0, 480.0, 1000.0, 2.0 ** 127, 0.0, 2.0 ** -12, 2.0 ** -10]
+    v = np.concatenate([mags, mid, below, above, extra])
+    v = np.concatenate([v, -v])
+    assert np.array_equal(_bf16_exact(v), v)  # every case is a bf16 value
+    return v
+
+
+@pytest.mark.parametrize("bmm2,o_scale", [(1.0, 1.0), (0.5, 4.0), (2.0, 0.25)])
+def test_fp8_output_encoding_exact(pkv, bmm2, o_scale):
+    # one key per request and q = 0: out = bmm2 * v[0] exactly, so the stored
+    # codes must be the oracle's encoding of bmm2 * v / o_scale, bit for bit
+    # (powers of two keep the scaling exact); NaN rows must come back NaN
+    v = _encode_cases()
+    v = np.concatenate([v, [np.nan, -np.nan]])
+    n_req = (v.size + 127) // 128
+    vals = np.zeros(n_req * 128)
+    vals[:v.size] = v
+    B, H, D, ps = n_req, 1, 128, 16
+    kv = torch.zeros(B, 2, H, ps, D, dtype=torch.bfloat16)
+    kv[:, 1, 0, 0, :] = torch.tensor(vals.reshape(B, D), dtype=torch.float64).to(torch.bfloat16)
+    q = torch.zeros(B, H, D, dtype=torch.bfloat16, device=DEV)
+    ws = torch.zeros(16, dtype=torch.uint8, device=DEV)
+    out = pkv.batch_decode_with_kv_cache(
+        q, kv.to(DEV), ws, torch.arange(B, dtype=torch.int32).reshape(B, 1).to(DEV),
+        torch.ones(B, dtype=torch.int32).to(DEV), 1, bmm1_scale=1.0, bmm2_scale=bmm2,
+        out_dtype=torch.float8_e4m3fn, o_scale=o_scale)
+    torch.cuda.synchronize()
+    got = out.view(torch.uint8).cpu().numpy().reshape(-1)
+    want = oracle.encode_e4m3fn(vals * bmm2 / o_scale)
+    # the accumulation starts from +0, so a zero comes back as +0 whatever
+    # the sign of v: zeros compare by value
+    nan, zero = np.isnan(vals), vals == 0
+    exact = ~nan & ~zero
+    bad = np.nonzero(got[exact] != want[exact])[0]
+    for i in bad[:8]:
+        print(f"v {vals[exact][i]!r}: got 0x{got[exact][i]:02x} want 0x{want[exact][i]:02x}")
+    assert bad.size == 0
+    assert np.all((got[zero] & 0x7F) == 0)
+    assert np.all((got[nan] & 0x7F) == 0x7F)
+
+
+def _e4m3_ulp(y):
+    """Spacing of e4m3fn values at magnitude y (subnormal spacing below 2^-6)."""
+    y = np.maximum(np.abs(y), 2.0 ** -6)
+    return np.exp2(np.floor(np.log2(y)) - 3)
+
+
+def check_fp8_out(out, ref, o_scale, atol=2e-2):
+    """Stored codes against the oracle: the unquantised values may differ by
+    atol, and the code then lies within one e4m3 spacing of the larger
+    magnitude (nearest rounding of a value at most atol away); references
+    beyond the format's range compare against the saturated value."""
+    dec = oracle.decode_bits(out.view(torch.uint8).cpu().numpy(), oracle.formats.E4M3) * o_scale
+    ref = np.clip(np.asarray(ref, dtype=np.float64), -448.0 * o_scale, 448.0 * o_scale)
+    tol = atol + _e4m3_ulp((np.abs(ref) + atol) / o_scale) * o_scale
+    err = np.abs(dec - ref)
+    assert np.all(err <= tol), float((err - tol).max())
+    return float(err.max())
+
+
+@pytest.mark.parametrize("seq,seed", [((1, 900), 80), ((3000, 9000), 81)])
+def test_fp8_output_against_oracle(pkv, seq, seed):
+    # short sequences take the single-split write, long ones the merge kernel
+    w = small(seed=seed, seq=seq, batch=4, q_len_per_req=3, window_left=2000, sinks=True,
+              num_qo_heads=8, num_kv_heads=2)
+    o_scale = 0.37
+    ws = torch.zeros(max(pkv.decode_workspace_size(4, 3, 8, 2, 128, w["max_seq_len"], 2000), 16),
+                     dtype=torch.uint8, device=DEV)
+    out = pkv.batch_decode_with_kv_cache(
+        w["query"], w["kv_cache"], ws, w["block_tables"].to(DEV), w["seq_lens"].to(DEV),
+        w["max_seq_len"], bmm1_scale=w["bmm1_scale"], bmm2_scale=1.7, window_left=2000,
+        sinks=w["sinks"].to(DEV), kv_layout=w["layout"], q_len_per_req=3,
+        out_dtype=torch.float8_e4m3fn, o_scale=o_scale)
+    torch.cuda.synchronize()
+    ref = oracle_decode(dict(w, bmm2_scale=1.7))
+    err = check_fp8_out(out, ref, o_scale)
+    print(f"max |dec(code) * o_scale - ref| {err:.3g}", flush=True)
+
+
+def test_device_tensor_scales_equal_float_scales(pkv):
+    w = small(seed=82, seq=(500, 6000), q_len_per_req=2, sinks=True, num_qo_heads=8,
+              num_kv_heads=2, kv_dtype=torch.float8_e4m3fn, page_size=32)
+    b1, b2 = 0.071, 1.9
+    a = run_decode(pkv, dict(w, bmm1_scale=b1, bmm2_scale=b2))
+    t1 = torch.tensor([b1], dtype=torch.float32, device=DEV)
+    t2 = torch.tensor([b2], dtype=torch.float32, device=DEV)
+    b = run_decode(pkv, dict(w, bmm1_scale=t1, bmm2_scale=t2))
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # a negative device bmm1 flips the query's sign inside the kernel
+    c = run_decode(pkv, dict(w, bmm1_scale=-b1, bmm2_scale=b2))
+    d = run_decode(pkv, dict(w, bmm1_scale=torch.tensor([-b1], device=DEV), bmm2_scale=t2))
+    assert torch.equal(c.view(torch.int16), d.view(torch.int16))
+    assert_out_close(d, oracle_decode(dict(w, bmm1_scale=-b1, bmm2_scale=b2)), d.dtype)

@@ -95,30 +95,34 @@ def test_decode_replays_with_new_lengths(pkv):
     ws = torch.zeros(max(pkv.decode_workspace_size(8, 2, 16, 4, 128, w["max_seq_len"], 700), 16),
                      dtype=torch.uint8, device=DEV)
     out_g = torch.empty_like(w["query"])
+    # bmm2 as a device tensor (the page's tensor form): its value changes
+    # between replays too
+    bmm2_d = torch.tensor([0.8], dtype=torch.float32, device=DEV)
 
-    def call(out):
+    def call(out, bmm2):
         pkv.batch_decode_with_kv_cache(w["query"], w["kv_cache"], ws, bt, seq_d,
                                        w["max_seq_len"], bmm1_scale=w["bmm1_scale"],
-                                       bmm2_scale=0.8, window_left=700, out=out, sinks=sinks,
+                                       bmm2_scale=bmm2, window_left=700, out=out, sinks=sinks,
                                        kv_layout="HND", q_len_per_req=2)
 
-    g = capture(lambda: call(out_g))
+    g = capture(lambda: call(out_g, bmm2_d))
     gen = torch.Generator().manual_seed(71)
-    for i in range(3):
+    for i, bmm2 in enumerate((0.8, 1.25, 0.5)):
         seq = seq0 if i == 0 else torch.randint(1, int(seq0.min()) + 1, (8,), generator=gen)
         seq_d.copy_(seq.to(torch.uint32))
+        bmm2_d.fill_(bmm2)
         w["query"].copy_(torch.randn(w["query"].shape, generator=gen).to(torch.bfloat16))
         out_g.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         out_e = torch.empty_like(out_g)
-        call(out_e)
+        call(out_e, bmm2)
         torch.cuda.synchronize()
-        print(f"replay {i}: seq {seq.tolist()}", flush=True)
+        print(f"replay {i}: seq {seq.tolist()} bmm2 {bmm2}", flush=True)
         assert torch.equal(out_g.view(torch.int16), out_e.view(torch.int16))
         if i == 1:
-            w2 = dict(w, seq_lens=seq.to(torch.uint32), bmm2_scale=0.8)
+            w2 = dict(w, seq_lens=seq.to(torch.uint32), bmm2_scale=bmm2)
             assert_out_close(out_g, oracle_decode(w2), torch.bfloat16)
 
 
