@@ -30,18 +30,31 @@ from .formats import decode_bits
 from .paging import gather_pages
 
 
-def allowed_mask(row_index, L_q, L_kv, causal, window_left=-1):
+def allowed_mask(row_index, L_q, L_kv, causal, window_left=-1, draft_mask=None):
     """allowed[r, j] for query rows ``row_index`` (0..L_q-1) and keys 0..L_kv-1.
 
     Bottom-right alignment: row t is at position pos = t + L_kv - L_q. With
     ``causal`` a key is allowed only if j <= pos; with window_left w >= 0 also
     only if j >= pos - w.
+
+    ``draft_mask`` (decode page, Parameters: ``mask``, the attention mask for
+    speculative decoding) is a boolean [L_q, L_q]: the L_q queries are drafts
+    at the last L_q positions, and draft t may see the draft at position
+    L_kv - L_q + i exactly when draft_mask[t, i]. It takes the place of the
+    causal rule among the drafts; keys before the drafts stay visible, and
+    the window still applies.
     """
     t = np.asarray(row_index, dtype=np.int64)[:, None]
     j = np.arange(L_kv, dtype=np.int64)[None, :]
     pos = t + (L_kv - L_q)
     ok = np.ones((t.shape[0], L_kv), dtype=bool)
-    if causal:
+    if draft_mask is not None:
+        dm = np.asarray(draft_mask, dtype=bool)
+        i = j - (L_kv - L_q)                     # draft index of key j
+        in_drafts = i >= 0
+        seen = dm[t, np.clip(i, 0, L_q - 1)]
+        ok &= ~in_drafts | seen
+    elif causal:
         ok &= j <= pos
     if window_left >= 0:
         ok &= j >= pos - window_left
@@ -49,7 +62,7 @@ def allowed_mask(row_index, L_q, L_kv, causal, window_left=-1):
 
 
 def attention(q, k, v, alpha, beta, causal, window_left=-1, sinks=None,
-              row_index=None, L_q=None):
+              row_index=None, L_q=None, draft_mask=None):
     """Softmax attention of one request.
 
     q [R, H_qo, d_qk], k [L_kv, H_kv, d_qk], v [L_kv, H_kv, d_vo], float64.
@@ -67,7 +80,7 @@ def attention(q, k, v, alpha, beta, causal, window_left=-1, sinks=None,
         row_index = np.arange(R)
     if L_q is None:
         L_q = R
-    ok = allowed_mask(row_index, L_q, L_kv, causal, window_left)
+    ok = allowed_mask(row_index, L_q, L_kv, causal, window_left, draft_mask)
     any_ok = ok.any(axis=1)
     out = np.zeros((R, H_qo, d_vo), dtype=np.float64)
     lse = np.full((R, H_qo), -np.inf, dtype=np.float64)
@@ -143,32 +156,48 @@ def batch_prefill(q, q_fmt, k_cache, v_cache, kv_fmt, block_tables,
 
 def batch_decode(query, q_fmt, k_cache, v_cache, kv_fmt, block_tables,
                  seq_lens, bmm1_scale, bmm2_scale, window_left, sinks,
-                 kv_layout, q_len_per_req=1, requests=None):
+                 kv_layout, q_len_per_req=1, requests=None, cum_seq_lens_q=None,
+                 spec_mask=None):
     """Batch decode over ``block_tables`` (decode page).
 
-    query: raw bits [batch * q_len_per_req, H_qo, d]; request b's queries are
-    its last q_len_per_req positions (rows b*q_len .. b*q_len + q_len - 1),
-    causal among themselves. Scores are bmm1_scale * q.k on the stored K
-    values; the output is bmm2_scale * softmax(.) V with the per-head
-    ``sinks`` logits in the denominator and the inclusive left window.
-    ``requests``: optional subset of request indices (output rows in order).
+    query: raw bits [num_tokens, H_qo, d]. Request b's queries are its last
+    q_len_b positions, causal among themselves: rows b*q_len_per_req ..
+    (q_len_b = q_len_per_req), or, with ``cum_seq_lens_q`` ([batch + 1],
+    the page's variable-length form), rows cum_seq_lens_q[b] ..
+    cum_seq_lens_q[b+1] - 1. ``spec_mask`` ([batch, Q, Q], Q the largest
+    query count) replaces the causal rule among a request's drafts: draft t
+    sees draft i when spec_mask[b, t, i] is nonzero (see ``allowed_mask``).
+    Scores are bmm1_scale * q.k on the stored K values; the output is
+    bmm2_scale * softmax(.) V with the per-head ``sinks`` logits in the
+    denominator and the inclusive left window. ``requests``: optional subset
+    of request indices (their rows, in order, are the output).
     Returns out [rows, H_qo, d].
     """
-    ql = q_len_per_req
+    B = len(seq_lens)
+    if cum_seq_lens_q is None:
+        cum = np.arange(B + 1, dtype=np.int64) * q_len_per_req
+    else:
+        cum = np.asarray(cum_seq_lens_q, dtype=np.int64)
     if requests is None:
-        requests = range(len(seq_lens))
+        requests = range(B)
     requests = list(requests)
     H_qo = query.shape[1]
     d_vo = v_cache.shape[-1]
-    out = np.zeros((len(requests) * ql, H_qo, d_vo))
-    for i, b in enumerate(requests):
+    n_out = sum(int(cum[b + 1] - cum[b]) for b in requests)
+    out = np.zeros((n_out, H_qo, d_vo))
+    r = 0
+    for b in requests:
+        ql = int(cum[b + 1] - cum[b])
         L_kv = int(seq_lens[b])
         kb = decode_bits(gather_pages(k_cache, block_tables[b], L_kv, kv_layout), kv_fmt)
         vb = decode_bits(gather_pages(v_cache, block_tables[b], L_kv, kv_layout), kv_fmt)
-        qb = decode_bits(query[b * ql:(b + 1) * ql], q_fmt)
+        qb = decode_bits(query[cum[b]:cum[b + 1]], q_fmt)
+        dm = None if spec_mask is None else np.asarray(spec_mask)[b, :ql, :ql] != 0
         o, _ = attention(qb, kb, vb, alpha=bmm1_scale, beta=bmm2_scale,
-                         causal=True, window_left=window_left, sinks=sinks)
-        out[i * ql:(i + 1) * ql] = o
+                         causal=True, window_left=window_left, sinks=sinks,
+                         draft_mask=dm)
+        out[r:r + ql] = o
+        r += ql
     return out
 
 

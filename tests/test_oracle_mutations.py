@@ -6,7 +6,9 @@ untouched) and checks that at least one independent pin rejects the
 mutant: torch's scaled-dot-product attention in float64 with a bottom-right
 mask built from tril / triu, a brute-force loop over the mask definition,
 or a closed form (sinks: o_sink = o * sigmoid(lse - sink); one allowed key:
-o = beta * v_j, lse = s_j).
+o = beta * v_j, lse = s_j); for the speculative-decoding draft mask and
+variable-length queries, reductions to the causal case, to key removal, and
+to one uniform call per request.
 """
 
 import os
@@ -35,6 +37,18 @@ MUTATIONS = {
     "output_scale_dropped": ("beta * o, 0.0)", "o, 0.0)"),
     "lse_base_2": ("m_s + np.log(np.where", "m_s + np.log2(np.where"),
     "not_normalised": ("o = (p @ v[:, kh, :]) / z[:, None]", "o = (p @ v[:, kh, :])"),
+    "draft_mask_transposed": ("seen = dm[t, np.clip(i, 0, L_q - 1)]",
+                              "seen = dm[np.clip(i, 0, L_q - 1), t]"),
+    "draft_mask_off_by_one": ("i = j - (L_kv - L_q)", "i = j - (L_kv - L_q) + 1"),
+    "draft_mask_and_causal": ("ok &= ~in_drafts | seen", "ok &= (~in_drafts | seen) & (j <= pos)"),
+    "draft_mask_hides_prefix": ("ok &= ~in_drafts | seen", "ok &= in_drafts & seen"),
+    "window_skipped_with_mask": ("    if window_left >= 0:\n        ok &= j >= pos - window_left",
+                                 "    if window_left >= 0 and draft_mask is None:\n"
+                                 "        ok &= j >= pos - window_left"),
+    "varlen_rows_uniform": ("qb = decode_bits(query[cum[b]:cum[b + 1]], q_fmt)",
+                            "qb = decode_bits(query[b * ql:(b + 1) * ql], q_fmt)"),
+    "varlen_mask_block": ("np.asarray(spec_mask)[b, :ql, :ql] != 0",
+                          "np.asarray(spec_mask)[b, -ql:, -ql:] != 0"),
 }
 
 
@@ -123,7 +137,112 @@ def pin_one_key(mod):
     return True
 
 
-PINS = [pin_sdpa, pin_brute_force_mask, pin_sinks_closed_form, pin_one_key]
+def pin_draft_mask_lower_triangle_is_causal(mod):
+    # a lower-triangular draft mask is the causal rule among the drafts
+    rng = np.random.default_rng(8)
+    for (L_q, L_kv, w) in [(4, 11, -1), (3, 9, 2), (4, 3, -1), (2, 7, 0)]:
+        tril = np.tril(np.ones((L_q, L_q), dtype=bool))
+        a = mod.allowed_mask(np.arange(L_q), L_q, L_kv, True, w, draft_mask=tril)
+        b = mod.allowed_mask(np.arange(L_q), L_q, L_kv, True, w)
+        if not np.array_equal(a, b):
+            return False
+        q = rng.standard_normal((L_q, 2, 16))
+        k = rng.standard_normal((L_kv, 1, 16))
+        v = rng.standard_normal((L_kv, 1, 8))
+        o1, _ = mod.attention(q, k, v, 0.3, 1.0, True, window_left=w, draft_mask=tril)
+        o2, _ = mod.attention(q, k, v, 0.3, 1.0, True, window_left=w)
+        if not np.array_equal(o1, o2):
+            return False
+    return True
+
+
+def pin_draft_mask_is_key_removal(mod):
+    # masking keys is the same as removing them: draft t's output equals a
+    # single unmasked query over the prefix plus the drafts its row allows
+    # (no window); random masks, not only trees
+    rng = np.random.default_rng(9)
+    for (L_q, L_kv) in [(4, 12), (5, 6), (3, 3)]:
+        dm = rng.random((L_q, L_q)) < 0.5
+        q = rng.standard_normal((L_q, 2, 16))
+        k = rng.standard_normal((L_kv, 1, 16))
+        v = rng.standard_normal((L_kv, 1, 8))
+        out, _ = mod.attention(q, k, v, 0.4, 1.5, True, draft_mask=dm)
+        d0 = L_kv - L_q
+        for t in range(L_q):
+            keep = [j for j in range(L_kv) if j < d0 or dm[t, j - d0]]
+            if not keep:
+                if not np.all(out[t] == 0):
+                    return False
+                continue
+            ref, _ = mod.attention(q[t:t + 1], k[keep], v[keep], 0.4, 1.5, False)
+            if not np.allclose(out[t], ref[0], rtol=1e-12, atol=1e-12):
+                return False
+    return True
+
+
+def pin_draft_mask_with_window_sdpa(mod):
+    # torch's float64 scaled-dot-product attention with the explicit mask:
+    # drafts by the draft mask, then the inclusive window on positions
+    rng = np.random.default_rng(10)
+    L_q, L_kv, w = 4, 10, 3
+    dm = rng.random((L_q, L_q)) < 0.6
+    np.fill_diagonal(dm, True)
+    m = torch.ones(L_q, L_kv, dtype=torch.bool)
+    m[:, L_kv - L_q:] = torch.from_numpy(dm)
+    m &= torch.ones(L_q, L_kv, dtype=torch.bool).triu(diagonal=L_kv - L_q - w)
+    q = rng.standard_normal((L_q, 1, 16))
+    k = rng.standard_normal((L_kv, 1, 16))
+    v = rng.standard_normal((L_kv, 1, 8))
+    ref = F.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2), torch.from_numpy(k).permute(1, 0, 2),
+        torch.from_numpy(v).permute(1, 0, 2), attn_mask=m, scale=0.5).permute(1, 0, 2).numpy()
+    out, _ = mod.attention(q, k, v, 0.5, 1.0, True, window_left=w, draft_mask=dm)
+    return np.allclose(out, ref, rtol=1e-10, atol=1e-10)
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def pin_varlen_rows(mod):
+    # ragged cum_seq_lens_q equals one uniform call per request with
+    # q_len_per_req = that request's query count; a spec_mask [B, Q, Q]
+    # uses each request's leading ql x ql block
+    rng = np.random.default_rng(11)
+    ps, H, d = 4, 2, 8
+    seq = np.array([9, 3, 6])
+    ql = np.array([3, 1, 2])
+    cum = np.concatenate([[0], np.cumsum(ql)])
+    n_pages = (seq + ps - 1) // ps
+    bt = np.full((3, int(n_pages.max())), -1, dtype=np.int64)
+    perm = rng.permutation(int(n_pages.sum()))
+    off = 0
+    for b in range(3):
+        bt[b, :n_pages[b]] = perm[off:off + n_pages[b]]
+        off += n_pages[b]
+    kc = _bf16_bits(rng.standard_normal((int(n_pages.sum()), H, ps, d)))
+    vc = _bf16_bits(rng.standard_normal((int(n_pages.sum()), H, ps, d)))
+    qry = _bf16_bits(rng.standard_normal((int(cum[-1]), 2 * H, d)))
+    mask = rng.random((3, 3, 3)) < 0.5
+    for b in range(3):
+        np.fill_diagonal(mask[b], True)
+    for sm in (None, mask):
+        got = mod.batch_decode(qry, "bf16", kc, vc, "bf16", bt, seq, 0.3, 1.0, -1, None, "HND",
+                               cum_seq_lens_q=cum, spec_mask=sm)
+        for b in range(3):
+            one = mod.batch_decode(qry[cum[b]:cum[b + 1]], "bf16", kc, vc, "bf16", bt[b:b + 1],
+                                   seq[b:b + 1], 0.3, 1.0, -1, None, "HND",
+                                   q_len_per_req=int(ql[b]),
+                                   spec_mask=None if sm is None else sm[b:b + 1, :ql[b], :ql[b]])
+            if not np.array_equal(got[cum[b]:cum[b + 1]], one):
+                return False
+    return True
+
+
+PINS = [pin_sdpa, pin_brute_force_mask, pin_sinks_closed_form, pin_one_key,
+        pin_draft_mask_lower_triangle_is_causal, pin_draft_mask_is_key_removal,
+        pin_draft_mask_with_window_sdpa, pin_varlen_rows]
 
 
 def test_pins_accept_the_oracle():
