@@ -221,12 +221,16 @@ def decode_workspace_size(batch_size, q_len_per_req, num_heads_qo, num_heads_kv,
 def batch_decode_with_kv_cache(query, kv_cache, workspace_buffer, block_tables, seq_lens,
                                max_seq_len, bmm1_scale=1.0, bmm2_scale=1.0, window_left=-1,
                                out=None, out_dtype=None, sinks=None, kv_layout="HND",
-                               q_len_per_req=1, o_scale=1.0):
+                               q_len_per_req=1, o_scale=1.0, mask=None, max_q_len=None,
+                               cum_seq_lens_q=None):
     """Batch decode over block_tables; returns out [num_tokens, num_heads, head_dim].
 
     bmm1_scale / bmm2_scale are floats or one-element float32 device tensors
     (read by the kernels at run time). With out_dtype torch.float8_e4m3fn each
     stored code is e4m3fn(out / o_scale) (nearest, ties to even, saturating).
+    cum_seq_lens_q ([batch + 1] int32) with max_q_len gives each request its
+    own query count; mask ([batch, Q, Q] bool or uint8) lets draft t see
+    draft i when mask[b, t, i] is set, in place of the causal rule.
     """
     layout = _layout(kv_layout)
     dev = query.device
@@ -236,9 +240,27 @@ def batch_decode_with_kv_cache(query, kv_cache, workspace_buffer, block_tables, 
         raise ValueError("query must be [num_tokens, num_heads, head_dim]")
     query = query.contiguous()
     h_qo = query.shape[1]
-    if query.shape[0] % int(q_len_per_req):
-        raise ValueError("num_tokens must be batch_size * q_len_per_req")
-    batch = query.shape[0] // int(q_len_per_req)
+    if (max_q_len is None) != (cum_seq_lens_q is None):
+        raise ValueError("max_q_len and cum_seq_lens_q must be given together")
+    cum = None
+    if cum_seq_lens_q is not None:
+        cum = _i32_on(cum_seq_lens_q, dev)
+        batch = cum.shape[0] - 1
+        q_max = int(max_q_len)
+    else:
+        if query.shape[0] % int(q_len_per_req):
+            raise ValueError("num_tokens must be batch_size * q_len_per_req")
+        batch = query.shape[0] // int(q_len_per_req)
+        q_max = int(q_len_per_req)
+    mask_ptr = None
+    if mask is not None:
+        if tuple(mask.shape) != (batch, q_max, q_max):
+            raise ValueError("mask must be [batch_size, Q, Q] with Q the query count per request")
+        if mask.dtype not in (torch.bool, torch.uint8) or mask.device != dev \
+                or not mask.is_contiguous():
+            raise ValueError("mask must be a contiguous bool or uint8 tensor on the "
+                             "query's device")
+        mask_ptr = mask.data_ptr()  # one byte per entry, nonzero = visible
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else query.dtype
     if out is None:
@@ -267,7 +289,8 @@ def batch_decode_with_kv_cache(query, kv_cache, workspace_buffer, block_tables, 
         workspace_buffer.numel() * workspace_buffer.element_size(), _ptr(bt), bt.shape[1],
         _ptr(seq), batch, int(max_seq_len), b1, b2, int(window_left), _ptr(out), _dt(out),
         sink_ptr, layout, int(q_len_per_req), h_qo, hkv, d, ps, _dt(query), _dt(k), b1_ptr,
-        b2_ptr, float(o_scale), None, 0, None, _stream()), "batch_decode_with_kv_cache")
+        b2_ptr, float(o_scale), None if cum is None else cum.data_ptr(),
+        0 if cum is None else q_max, mask_ptr, _stream()), "batch_decode_with_kv_cache")
     return out
 
 

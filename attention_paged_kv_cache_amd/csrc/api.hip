@@ -289,9 +289,10 @@ PKV_API pkv_status pkv_batch_decode_with_kv_cache(
     int32_t max_q_len, const uint8_t *spec_mask, void *stream) {
   CHECK(batch_size >= 0, PKV_ERR_INVALID_ARG, "batch_size < 0");
   CHECK(q_len_per_req >= 1, PKV_ERR_INVALID_ARG, "q_len_per_req < 1");
-  CHECK(cum_seq_lens_q == nullptr && max_q_len == 0 && spec_mask == nullptr,
-        PKV_ERR_UNSUPPORTED,
-        "variable-length queries and the speculative-decoding mask are not supported");
+  CHECK(cum_seq_lens_q ? max_q_len >= 1 : max_q_len == 0, PKV_ERR_INVALID_ARG,
+        "max_q_len must be >= 1 with cum_seq_lens_q and 0 without it");
+  // queries per request, or their maximum with variable-length queries
+  const int32_t q_max = cum_seq_lens_q ? max_q_len : q_len_per_req;
   CHECK(window_left >= -1, PKV_ERR_INVALID_ARG, "window_left < -1");
   CHECK(num_heads_kv > 0 && num_heads_qo > 0, PKV_ERR_INVALID_ARG,
         "head counts must be positive");
@@ -300,9 +301,8 @@ PKV_API pkv_status pkv_batch_decode_with_kv_cache(
   CHECK(num_heads_qo % num_heads_kv == 0, PKV_ERR_UNSUPPORTED,
         "num_heads_qo must be a multiple of num_heads_kv");
   CHECK(head_dim == 128, PKV_ERR_UNSUPPORTED, "head_dim must be 128");
-  CHECK((int64_t)q_len_per_req * (num_heads_qo / num_heads_kv) <= 64,
-        PKV_ERR_UNSUPPORTED,
-        "q_len_per_req * num_heads_qo / num_heads_kv must be <= 64");
+  CHECK((int64_t)q_max * (num_heads_qo / num_heads_kv) <= 64, PKV_ERR_UNSUPPORTED,
+        "q_len_per_req (or max_q_len) * num_heads_qo / num_heads_kv must be <= 64");
   CHECK(kv_layout == PKV_NHD || kv_layout == PKV_HND, PKV_ERR_INVALID_ARG,
         "kv_layout must be NHD or HND");
   CHECK(q_dtype == PKV_F16 || q_dtype == PKV_BF16, PKV_ERR_UNSUPPORTED,
@@ -326,7 +326,7 @@ PKV_API pkv_status pkv_batch_decode_with_kv_cache(
   CHECK((page_stride_k * es) % 16 == 0 && (page_stride_v * es) % 16 == 0,
         PKV_ERR_UNSUPPORTED, "page strides must be multiples of 16 bytes");
   const pkv::DecodePlan plan =
-      pkv::plan_decode(batch_size, q_len_per_req, num_heads_qo, num_heads_kv,
+      pkv::plan_decode(batch_size, q_max, num_heads_qo, num_heads_kv,
                        head_dim, max_seq_len, window_left);
   CHECK(workspace_bytes >= plan.workspace_bytes, PKV_ERR_WORKSPACE_TOO_SMALL,
         "workspace smaller than pkv_decode_workspace_size(...)");
@@ -365,7 +365,9 @@ PKV_API pkv_status pkv_batch_decode_with_kv_cache(
   a.window_left = window_left;
   a.out = out;
   a.sinks = sinks;
-  a.q_len = q_len_per_req;
+  a.q_len = q_max;
+  a.cum_q = cum_seq_lens_q;
+  a.mask = spec_mask;
   a.num_heads_qo = num_heads_qo;
   a.num_heads_kv = num_heads_kv;
   a.head_dim = head_dim;

@@ -84,10 +84,22 @@ __device__ __forceinline__ u32x4 load_run(const char *p) {
 // rounded down to a multiple of 32 so that every 32-key step starts on a
 // page boundary for page sizes 16, 32 and 64. Keys below the true left edge
 // are masked like any other key outside the window.
-__device__ __forceinline__ int key_origin(const DecodeArgs &a, int seq) {
+__device__ __forceinline__ int key_origin(const DecodeArgs &a, int seq, int ql) {
   int lo = 0;
-  if (a.window_left >= 0) lo = max(0, seq - a.q_len - a.window_left);
+  if (a.window_left >= 0) lo = max(0, seq - ql - a.window_left);
   return lo & ~31;
+}
+
+// Request b's query count and first query row: uniform q_len, or from the
+// variable-length offsets.
+__device__ __forceinline__ void request_rows(const DecodeArgs &a, int b, int &ql, int &row0) {
+  if (a.cum_q) {
+    row0 = a.cum_q[b];
+    ql = a.cum_q[b + 1] - row0;
+  } else {
+    row0 = b * a.q_len;
+    ql = a.q_len;
+  }
 }
 
 // Raw K/V of one 32-key step as loaded (e4m3 bytes or 16-bit values).
@@ -120,6 +132,9 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
   __shared__ float sh_m[kWaves][R];
   __shared__ float sh_l[kWaves][R];
   __shared__ float sh_o[R][kD + 4];
+  // each row's draft mask as bits (bit i: draft i visible), when a mask is
+  // given; read only on the steps that reach the drafts
+  __shared__ uint64_t sh_mbits[R];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -132,7 +147,10 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
   const int b = (blockIdx.x / a.num_heads_kv) % a.batch;
   const int kvh = blockIdx.x % a.num_heads_kv;
   const int seq = (int)a.seq_lens[b];
-  const int lo = key_origin(a, seq);
+  int ql, qrow0;
+  request_rows(a, b, ql, qrow0);
+  if (ql <= 0) return;
+  const int lo = key_origin(a, seq, ql);
   const int k_begin = lo + split * chunk;
   if (k_begin >= seq) return;
   const int k_end = min(seq, k_begin + chunk);
@@ -142,7 +160,12 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
   const int w_end = min(k_end, w_begin + cw);
 
   const int G = a.num_heads_qo / a.num_heads_kv;
-  const int rows = a.q_len * G;
+  const int rows = ql * G;            // this request's rows
+  const int rows_ws = a.q_len * G;    // workspace rows per unit (the maximum)
+  // With a draft mask, keys from the first draft on are allowed by the
+  // mask; keys before it only by the window.
+  const int dstart = seq - ql;
+  const int mask_from = a.mask ? dstart : 0x7fffffff;
   const float bmm1 = a.bmm1_ptr ? a.bmm1_ptr[0] : a.bmm1_scale;
   const float c_raw = bmm1 * kLog2e;
   const bool negate = c_raw < 0.0f;
@@ -156,10 +179,13 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
     const int n = nb * 16 + r16;
     const int qi = n / G, g = n - qi * G;
     const bool ok = n < rows;
-    pos[nb] = ok ? seq - a.q_len + qi : -1;  // last allowed key
-    wlo[nb] = (a.window_left >= 0) ? pos[nb] - a.window_left : 0;
+    const int qpos = seq - ql + qi;  // the query's position
+    // last allowed key (padding rows: none); with a mask every key up to
+    // the end is a candidate and the mask decides among the drafts
+    pos[nb] = ok ? (a.mask ? seq - 1 : qpos) : -1;
+    wlo[nb] = (a.window_left >= 0) ? qpos - a.window_left : 0;
     const char *qp = (const char *)a.q +
-                     ((int64_t)(b * a.q_len + qi) * a.num_heads_qo + kvh * G + g) * kD * 2;
+                     ((int64_t)(qrow0 + qi) * a.num_heads_qo + kvh * G + g) * kD * 2;
     const uint32_t flip = negate ? 0x80008000u : 0u;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -169,6 +195,19 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
       qop[nb][s] = v;
     }
   }
+  if (a.mask) {  // uniform: every thread takes the barrier or none does
+    if (tid < R) {
+      uint64_t bits = 0;
+      if (tid < rows) {  // ql <= 64 because rows = ql * G <= 64
+        const uint8_t *mrow = a.mask + ((int64_t)b * a.q_len + tid / G) * a.q_len;
+        for (int i = 0; i < ql; ++i)
+          if (mrow[i]) bits |= 1ull << i;
+      }
+      sh_mbits[tid] = bits;
+    }
+    __syncthreads();
+  }
+
   // bounds over the real rows only (padding rows have pos = -1)
   int pos_min = 0x7fffffff, wlo_max = -0x7fffffff;
 #pragma unroll
@@ -282,7 +321,7 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
     // ---- mask where the step crosses a boundary ----------------------------
     // lane holds keys kg0 + 8*g4 + 4*mb + i for its row
     const bool clean = (kg0 + 32 <= w_end) && (kg0 >= w_begin) && (kg0 >= wlo_max) &&
-                       (kg0 + 31 <= pos_min);
+                       (kg0 + 31 <= pos_min) && (kg0 + 32 <= mask_from);
     if (!clean) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -291,7 +330,12 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = kg0 + 8 * g4 + 4 * mb + i;
-            if (key >= w_end || key < w_begin || key > pos[nb] || key < wlo[nb])
+            // a draft key (key >= mask_from, so 0 <= key - dstart < ql for
+            // keys inside the sequence) must have its mask bit set
+            const uint32_t di = (uint32_t)(key - dstart);
+            const bool hidden = key >= mask_from &&
+                                !(di < 64u && ((sh_mbits[nb * 16 + r16] >> di) & 1ull));
+            if (key >= w_end || key < w_begin || key > pos[nb] || key < wlo[nb] || hidden)
               sacc[mb][nb][i] = -INFINITY;
           }
     }
@@ -410,7 +454,7 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
   }
 
   // ---- write: final output (single split) or partial ------------------------------
-  const int n_rows = rows;
+  const int n_rows = rows;  // only this request's rows are written
   const bool direct = n_splits == 1;
   for (int idx = tid; idx < n_rows * (kD / 4); idx += kThreads) {
     const int n = idx / (kD / 4);
@@ -427,7 +471,7 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
       float den = L;
       if (a.sinks) den += fast_exp2(a.sinks[head] * kLog2e - M_use);
       const float bmm2 = a.bmm2_ptr ? a.bmm2_ptr[0] : a.bmm2_scale;
-      const int64_t orow = (int64_t)(b * a.q_len + qi) * a.num_heads_qo + head;
+      const int64_t orow = (int64_t)(qrow0 + qi) * a.num_heads_qo + head;
       if (a.out_dtype == 2) {
         const float scale = den > 0.0f ? bmm2 / (den * a.o_scale) : 0.0f;
         const uint32_t w = e4m3_encode(src[0] * scale) | (e4m3_encode(src[1] * scale) << 8) |
@@ -449,11 +493,11 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
       }
     } else {
       const int64_t unit = ((int64_t)b * a.num_heads_kv + kvh) * max_splits + split;
-      float *dst = ws_o + (unit * rows + n) * kD + d4;
+      float *dst = ws_o + (unit * rows_ws + n) * kD + d4;
       *reinterpret_cast<f32x4 *>(dst) = f32x4{src[0], src[1], src[2], src[3]};
       if (d4 == 0) {
-        ws_ml[(unit * rows + n) * 2 + 0] = M;
-        ws_ml[(unit * rows + n) * 2 + 1] = L;
+        ws_ml[(unit * rows_ws + n) * 2 + 0] = M;
+        ws_ml[(unit * rows_ws + n) * 2 + 1] = L;
       }
     }
   }
@@ -466,7 +510,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a,
                                                            const float *__restrict__ ws_o,
                                                            const float *__restrict__ ws_ml) {
   const int G = a.num_heads_qo / a.num_heads_kv;
-  const int rows = a.q_len * G;
+  const int rows = a.q_len * G;  // workspace rows per unit (the maximum)
   const int gw = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int total = a.batch * a.num_heads_kv * rows;
@@ -474,12 +518,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a,
   const int n = gw % rows;
   const int kvh = (gw / rows) % a.num_heads_kv;
   const int b = gw / (rows * a.num_heads_kv);
+  int ql, qrow0;
+  request_rows(a, b, ql, qrow0);
+  if (n >= ql * G) return;
   const int seq = (int)a.seq_lens[b];
-  const int lo = key_origin(a, seq);
+  const int lo = key_origin(a, seq, ql);
   const int n_splits = seq > lo ? (seq - lo + chunk - 1) / chunk : 0;
   const int qi = n / G, g = n - qi * G;
   const int head = kvh * G + g;
-  const int64_t orow = (int64_t)(b * a.q_len + qi) * a.num_heads_qo + head;
+  const int64_t orow = (int64_t)(qrow0 + qi) * a.num_heads_qo + head;
   if (n_splits == 1) return;  // written by the split kernel
   const int64_t unit0 = ((int64_t)b * a.num_heads_kv + kvh) * max_splits;
   float M = -INFINITY;

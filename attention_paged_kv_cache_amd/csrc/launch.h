@@ -73,8 +73,11 @@ struct DecodeArgs {
   int32_t window_left;
   void *out;
   const float *sinks;
+  // q_len: queries per request, or their maximum when cum_q is given
   int32_t q_len, num_heads_qo, num_heads_kv, head_dim, page_size;
   int32_t q_dtype, kv_dtype, out_dtype;  // pkv_dtype values
+  const int32_t *cum_q;  // [batch + 1] query row offsets, or null (uniform q_len)
+  const uint8_t *mask;   // [batch][q_len][q_len] draft mask, or null (causal)
   void *workspace;
 };
 // Split plan shared by the workspace-size query and the launcher.

@@ -210,13 +210,22 @@ size_t pkv_decode_workspace_size(int32_t batch_size, int32_t q_len_per_req,
  *         of the two scales), read by the kernels at run time
  *   seq_lens [batch_size] uint32; max_seq_len >= every entry
  *   sinks    [num_heads_qo] float32 logits or NULL
- *   cum_seq_lens_q, max_q_len, spec_mask  variable-length queries and the
- *         speculative-decoding mask (decode page, Parameters); must be NULL,
- *         0 and NULL in this version (PKV_ERR_UNSUPPORTED otherwise)
+ *   cum_seq_lens_q, max_q_len  variable-length queries (decode page,
+ *         Parameters): when cum_seq_lens_q ([batch_size + 1] int32 on the
+ *         device) is given, request b's queries are query/out rows
+ *         cum_seq_lens_q[b] .. cum_seq_lens_q[b+1] - 1 (its last that many
+ *         positions, any count from 0 to max_q_len >= 1) and q_len_per_req
+ *         is ignored; otherwise max_q_len must be 0
+ *   spec_mask  the speculative-decoding mask (decode page, Parameters) or
+ *         NULL: uint8 [batch_size][Q][Q] on the device, Q = max_q_len with
+ *         cum_seq_lens_q, else q_len_per_req. Draft t of request b sees the
+ *         draft at position seq_lens[b] - q_b + i when
+ *         spec_mask[b][t][i] != 0 (q_b its query count); this replaces the
+ *         causal rule among the drafts. Keys before the drafts stay visible,
+ *         and window_left still applies (to positions).
  *   workspace >= pkv_decode_workspace_size(...) bytes (contents ignored)
  * Supported: head_dim == 128, num_heads_qo % num_heads_kv == 0,
- * q_len_per_req * num_heads_qo / num_heads_kv <= 64, page_size in
- * {16, 32, 64}.
+ * Q * num_heads_qo / num_heads_kv <= 64, page_size in {16, 32, 64}.
  */
 pkv_status pkv_batch_decode_with_kv_cache(
     const void *query, const void *k_cache, const void *v_cache,

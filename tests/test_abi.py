@@ -103,8 +103,9 @@ def _decode(lib, **over):
     (dict(odt=2, o_scale=float("inf")), "o_scale"),
     (dict(odt=2, o_scale=float("nan")), "o_scale"),
     (dict(odt=7), "output dtype"),
-    (dict(cum_q=FAKE), "variable-length"),
-    (dict(mask=FAKE), "variable-length"),
+    (dict(cum_q=FAKE, max_q=0), "max_q_len"),
+    (dict(cum_q=None, max_q=3), "max_q_len"),
+    (dict(cum_q=FAKE, max_q=17, hqo=32, hkv=8), "<= 64"),
 ])
 def test_decode_validation(lib, over, needle):
     st = _decode(lib, **over)

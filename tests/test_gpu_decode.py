@@ -304,3 +304,122 @@ def test_device_tensor_scales_equal_float_scales(pkv):
     d = run_decode(pkv, dict(w, bmm1_scale=torch.tensor([-b1], device=DEV), bmm2_scale=t2))
     assert torch.equal(c.view(torch.int16), d.view(torch.int16))
     assert_out_close(d, oracle_decode(dict(w, bmm1_scale=-b1, bmm2_scale=b2)), d.dtype)
+
+
+# ---- variable-length queries and the speculative-decoding mask ----------------
+
+def oracle_decode_ragged(w, cum, mask=None):
+    from workloads import compact_pages
+    seq = w["seq_lens"].to(torch.int64)
+    used = [(int(s) + w["page_size"] - 1) // w["page_size"] for s in seq]
+    sub, bt = compact_pages(w["kv_cache"], w["block_tables"], used)
+    sinks = None if w["sinks"] is None else w["sinks"].double().numpy()
+    return oracle.batch_decode(
+        bits(w["query"]), oracle.formats.BF16, bits(sub[:, 0]), bits(sub[:, 1]),
+        oracle.formats.E4M3 if w["kv_cache"].dtype == torch.float8_e4m3fn else oracle.formats.BF16,
+        bt.numpy(), seq.numpy(), w["bmm1_scale"], w["bmm2_scale"], w["window_left"], sinks,
+        w["layout"], cum_seq_lens_q=cum, spec_mask=None if mask is None else mask.cpu().numpy())
+
+
+def run_ragged(pkv, w, cum, q_max, mask=None, out=None):
+    B = w["seq_lens"].shape[0]
+    ws = torch.zeros(max(pkv.decode_workspace_size(
+        B, q_max, w["num_qo_heads"], w["num_kv_heads"], 128, w["max_seq_len"],
+        w["window_left"]), 16), dtype=torch.uint8, device=DEV)
+    sinks = None if w["sinks"] is None else w["sinks"].to(DEV)
+    r = pkv.batch_decode_with_kv_cache(
+        w["query"], w["kv_cache"], ws, w["block_tables"].to(DEV), w["seq_lens"].to(DEV),
+        w["max_seq_len"], bmm1_scale=w["bmm1_scale"], bmm2_scale=w["bmm2_scale"],
+        window_left=w["window_left"], sinks=sinks, kv_layout=w["layout"], out=out,
+        mask=mask, max_q_len=None if cum is None else q_max,
+        cum_seq_lens_q=None if cum is None else torch.tensor(cum, dtype=torch.int32, device=DEV),
+        q_len_per_req=w["q_len_per_req"] if cum is None else 1)
+    torch.cuda.synchronize()
+    return r
+
+
+@pytest.mark.parametrize("seq,kv_dtype,window,seed", [
+    ((1, 900), torch.bfloat16, -1, 90),
+    ((3000, 9000), torch.bfloat16, 2500, 91),
+    ((200, 5000), torch.float8_e4m3fn, 300, 92),
+])
+def test_variable_length_queries(pkv, seq, kv_dtype, window, seed):
+    # ragged query counts 0..4 per request (empty requests included); the
+    # rows past the last query are never written
+    q_max = 4
+    w = small(seed=seed, seq=seq, batch=7, q_len_per_req=q_max, window_left=window, sinks=True,
+              num_qo_heads=16, num_kv_heads=4, kv_dtype=kv_dtype, page_size=32)
+    counts = np.random.default_rng(seed).integers(0, q_max + 1, size=7)
+    counts[2] = 0
+    cum = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    out = torch.full_like(w["query"], float("nan"))
+    got = run_ragged(pkv, w, cum, q_max, out=out)
+    n = int(cum[-1])
+    ref = oracle_decode_ragged(w, cum)
+    err = assert_out_close(got[:n], ref, got.dtype)
+    assert torch.isnan(got[n:].float()).all()
+    print(f"counts {counts.tolist()} max |out err| {err:.3g}", flush=True)
+
+
+def test_uniform_offsets_equal_fixed_query_count(pkv):
+    w = small(seed=93, seq=(100, 6000), batch=5, q_len_per_req=3, window_left=1000, sinks=True,
+              num_qo_heads=8, num_kv_heads=2)
+    a = run_decode(pkv, w)
+    cum = (np.arange(6) * 3).astype(np.int32)
+    b = run_ragged(pkv, w, cum, 3)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def _tree_mask(B, Q, rng):
+    # each draft's parent is an earlier draft (or the prefix); a draft sees
+    # itself and its ancestors
+    m = np.zeros((B, Q, Q), dtype=bool)
+    for b in range(B):
+        parent = [-1] + [int(rng.integers(-1, i)) for i in range(1, Q)]
+        for t in range(Q):
+            a = t
+            while a >= 0:
+                m[b, t, a] = True
+                a = parent[a]
+    return m
+
+
+@pytest.mark.parametrize("kind,window,seed", [("tree", -1, 94), ("random", 40, 95),
+                                              ("tree", 3, 96)])
+def test_spec_mask(pkv, kind, window, seed):
+    Q = 4
+    w = small(seed=seed, seq=(2, 3000), batch=6, q_len_per_req=Q, window_left=window,
+              sinks=True, num_qo_heads=16, num_kv_heads=2)
+    rng = np.random.default_rng(seed)
+    m = _tree_mask(6, Q, rng) if kind == "tree" else rng.random((6, Q, Q)) < 0.5
+    mask = torch.from_numpy(m).to(DEV)
+    got = run_ragged(pkv, w, None, Q, mask=mask)
+    cum = (np.arange(7) * Q).astype(np.int32)
+    ref = oracle_decode_ragged(w, cum, mask)
+    err = assert_out_close(got, ref, got.dtype)
+    print(f"{kind} mask max |out err| {err:.3g}", flush=True)
+
+
+def test_lower_triangular_mask_equals_causal(pkv):
+    Q = 4
+    w = small(seed=97, seq=(50, 7000), batch=5, q_len_per_req=Q, window_left=-1, sinks=True,
+              num_qo_heads=8, num_kv_heads=2)
+    tril = torch.ones(5, Q, Q, dtype=torch.bool).tril().to(DEV)
+    a = run_decode(pkv, w)
+    b = run_ragged(pkv, w, None, Q, mask=tril)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_spec_mask_with_variable_length_queries(pkv):
+    q_max = 4
+    w = small(seed=98, seq=(5, 4000), batch=6, q_len_per_req=q_max, window_left=500, sinks=True,
+              num_qo_heads=8, num_kv_heads=2, kv_dtype=torch.float8_e4m3fn, page_size=16)
+    rng = np.random.default_rng(98)
+    counts = rng.integers(1, q_max + 1, size=6)
+    cum = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    m = rng.random((6, q_max, q_max)) < 0.5
+    mask = torch.from_numpy(m).to(DEV)
+    got = run_ragged(pkv, w, cum, q_max, mask=mask)
+    n = int(cum[-1])
+    ref = oracle_decode_ragged(w, cum, mask)
+    assert_out_close(got[:n], ref, got.dtype)
