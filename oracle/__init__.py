@@ -33,6 +33,7 @@ from .attention import (
     allowed_mask,
     attention,
     batch_prefill,
+    batch_prefill_ragged,
     batch_decode,
     allowed_pairs,
     keys_read,

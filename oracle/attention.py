@@ -154,6 +154,44 @@ def batch_prefill(q, q_fmt, k_cache, v_cache, kv_fmt, block_tables,
     return out, lse
 
 
+def batch_prefill_ragged(q, q_fmt, k, v, kv_fmt, seq_lens_q, seq_lens_kv, scale,
+                         causal, q_scale=1.0, k_scale=1.0, v_scale=1.0,
+                         offsets_q=None, offsets_o=None, offsets_k=None, offsets_v=None,
+                         offsets_stats=None, out_rows=None):
+    """Batch prefill without paging (prefill page: k_cache / v_cache of shape
+    (total KV length, H_kv, d) when paging is off; batch_offsets_q/o/k/v/
+    stats). Request b's L_q query rows start at row offsets_q[b] of q, its
+    L_kv key and value rows at offsets_k[b] / offsets_v[b] of k / v, and its
+    output and LSE rows at offsets_o[b] / offsets_stats[b]. An absent offset
+    array is the exclusive prefix sum of the lengths (rows packed in request
+    order). Offsets count rows (tokens). q, k, v are raw bits.
+    Returns (out [out_rows, H_qo, d_vo], lse [out_rows, H_qo]); rows no
+    request writes are NaN. out_rows defaults to sum L_q.
+    """
+    B = len(seq_lens_q)
+    cq = _exclusive_cumsum(seq_lens_q)
+    ck = _exclusive_cumsum(seq_lens_kv)
+    pick = lambda off, dflt: dflt[:B] if off is None else np.asarray(off, dtype=np.int64)
+    oq, oo = pick(offsets_q, cq), pick(offsets_o, cq)
+    ok_, ov = pick(offsets_k, ck), pick(offsets_v, ck)
+    os_ = pick(offsets_stats, cq)
+    n = int(cq[-1]) if out_rows is None else int(out_rows)
+    H_qo, d_vo = q.shape[1], v.shape[-1]
+    out = np.full((n, H_qo, d_vo), np.nan)
+    lse = np.full((n, H_qo), np.nan)
+    for b in range(B):
+        L_q, L_kv = int(seq_lens_q[b]), int(seq_lens_kv[b])
+        if L_q == 0:
+            continue
+        qb = decode_bits(q[oq[b]:oq[b] + L_q], q_fmt) * q_scale
+        kb = decode_bits(k[ok_[b]:ok_[b] + L_kv], kv_fmt) * k_scale
+        vb = decode_bits(v[ov[b]:ov[b] + L_kv], kv_fmt) * v_scale
+        o, l = attention(qb, kb, vb, alpha=scale, beta=1.0, causal=causal)
+        out[oo[b]:oo[b] + L_q] = o
+        lse[os_[b]:os_[b] + L_q] = l
+    return out, lse
+
+
 def batch_decode(query, q_fmt, k_cache, v_cache, kv_fmt, block_tables,
                  seq_lens, bmm1_scale, bmm2_scale, window_left, sinks,
                  kv_layout, q_len_per_req=1, requests=None, cum_seq_lens_q=None,

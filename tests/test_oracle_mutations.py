@@ -49,6 +49,14 @@ MUTATIONS = {
                             "qb = decode_bits(query[b * ql:(b + 1) * ql], q_fmt)"),
     "varlen_mask_block": ("np.asarray(spec_mask)[b, :ql, :ql] != 0",
                           "np.asarray(spec_mask)[b, -ql:, -ql:] != 0"),
+    "ragged_k_at_q_offsets": ("kb = decode_bits(k[ok_[b]:ok_[b] + L_kv], kv_fmt)",
+                              "kb = decode_bits(k[oq[b]:oq[b] + L_kv], kv_fmt)"),
+    "ragged_v_at_k_offsets": ("vb = decode_bits(v[ov[b]:ov[b] + L_kv], kv_fmt)",
+                              "vb = decode_bits(v[ok_[b]:ok_[b] + L_kv], kv_fmt)"),
+    "ragged_out_at_q_offsets": ("out[oo[b]:oo[b] + L_q] = o", "out[oq[b]:oq[b] + L_q] = o"),
+    "ragged_lse_at_out_offsets": ("lse[os_[b]:os_[b] + L_q] = l", "lse[oo[b]:oo[b] + L_q] = l"),
+    "ragged_kv_packed_by_q_lens": ("ck = _exclusive_cumsum(seq_lens_kv)",
+                                   "ck = _exclusive_cumsum(seq_lens_q)"),
 }
 
 
@@ -240,9 +248,90 @@ def pin_varlen_rows(mod):
     return True
 
 
+def _ragged_case(rng):
+    lq = np.array([5, 0, 3, 7])
+    lkv = lq + np.array([4, 2, 0, 9])
+    H_qo, H_kv, d = 4, 2, 8
+    q = _bf16_bits(rng.standard_normal((int(lq.sum()), H_qo, d)))
+    k = _bf16_bits(rng.standard_normal((int(lkv.sum()), H_kv, d)))
+    v = _bf16_bits(rng.standard_normal((int(lkv.sum()), H_kv, d)))
+    return lq, lkv, q, k, v
+
+
+def pin_ragged_equals_paged(mod):
+    # the packed non-paged layout is the paged one with its pages gathered:
+    # scatter each request's rows into 4-token pages in shuffled order and the
+    # paged prefill must return the same values
+    rng = np.random.default_rng(12)
+    lq, lkv, q, k, v = _ragged_case(rng)
+    ps = 4
+    n_pages = (lkv + ps - 1) // ps
+    perm = rng.permutation(int(n_pages.sum()))
+    bt = np.full((4, int(n_pages.max())), -1, dtype=np.int64)
+    kc = np.zeros((int(n_pages.sum()), ps, 2, 8), dtype=np.uint16)
+    vc = np.zeros_like(kc)
+    ck = np.concatenate([[0], np.cumsum(lkv)])
+    off = 0
+    for b in range(4):
+        for p in range(n_pages[b]):
+            page = perm[off + p]
+            bt[b, p] = page
+            rows = range(p * ps, min((p + 1) * ps, int(lkv[b])))
+            for j in rows:
+                kc[page, j - p * ps] = k[ck[b] + j]
+                vc[page, j - p * ps] = v[ck[b] + j]
+        off += n_pages[b]
+    o1, l1 = mod.batch_prefill_ragged(q, "bf16", k, v, "bf16", lq, lkv, 0.3, True)
+    o2, l2 = mod.batch_prefill(q, "bf16", kc, vc, "bf16", bt, lq, lkv, 0.3, True, "NHD")
+    return np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def pin_ragged_offsets_move_rows(mod):
+    # explicit offsets that store the requests in another order with gaps
+    # between them give the packed result, moved to those rows
+    rng = np.random.default_rng(13)
+    lq, lkv, q, k, v = _ragged_case(rng)
+    o_ref, l_ref = mod.batch_prefill_ragged(q, "bf16", k, v, "bf16", lq, lkv, 0.3, True)
+    order = [2, 0, 3, 1]
+    def place(lens, gap):
+        offs, cur = np.zeros(4, dtype=np.int64), 0
+        for b in order:
+            offs[b] = cur
+            cur += int(lens[b]) + gap
+        return offs, cur
+    oq, nq = place(lq, 2)
+    oo, no = place(lq, 3)
+    os_, ns = place(lq, 1)
+    ok_, nk = place(lkv, 5)
+    ov, nv = place(lkv, 1)
+    cq = np.concatenate([[0], np.cumsum(lq)])
+    ck = np.concatenate([[0], np.cumsum(lkv)])
+    q2 = np.zeros((nq,) + q.shape[1:], dtype=q.dtype)
+    k2 = np.zeros((nk,) + k.shape[1:], dtype=k.dtype)
+    v2 = np.zeros((nv,) + v.shape[1:], dtype=v.dtype)
+    for b in range(4):
+        q2[oq[b]:oq[b] + lq[b]] = q[cq[b]:cq[b + 1]]
+        k2[ok_[b]:ok_[b] + lkv[b]] = k[ck[b]:ck[b + 1]]
+        v2[ov[b]:ov[b] + lkv[b]] = v[ck[b]:ck[b + 1]]
+    o, _ = mod.batch_prefill_ragged(q2, "bf16", k2, v2, "bf16", lq, lkv, 0.3, True,
+                                    offsets_q=oq, offsets_o=oo, offsets_k=ok_, offsets_v=ov,
+                                    offsets_stats=os_, out_rows=max(no, ns))
+    _, l = mod.batch_prefill_ragged(q2, "bf16", k2, v2, "bf16", lq, lkv, 0.3, True,
+                                    offsets_q=oq, offsets_o=oo, offsets_k=ok_, offsets_v=ov,
+                                    offsets_stats=os_, out_rows=max(no, ns))
+    for b in range(4):
+        if not np.array_equal(o[oo[b]:oo[b] + lq[b]], o_ref[cq[b]:cq[b + 1]]):
+            return False
+        if not np.array_equal(l[os_[b]:os_[b] + lq[b]], l_ref[cq[b]:cq[b + 1]]):
+            return False
+    written = sum(int(x) for x in lq)
+    return int(np.isfinite(o[:, 0, 0]).sum()) == written
+
+
 PINS = [pin_sdpa, pin_brute_force_mask, pin_sinks_closed_form, pin_one_key,
         pin_draft_mask_lower_triangle_is_causal, pin_draft_mask_is_key_removal,
-        pin_draft_mask_with_window_sdpa, pin_varlen_rows]
+        pin_draft_mask_with_window_sdpa, pin_varlen_rows, pin_ragged_equals_paged,
+        pin_ragged_offsets_move_rows]
 
 
 def test_pins_accept_the_oracle():
@@ -251,8 +340,16 @@ def test_pins_accept_the_oracle():
         assert pin(mod), pin.__name__
 
 
+def passes(pin, mod):
+    """A pin rejects a mutant by returning False or by the mutant raising."""
+    try:
+        return bool(pin(mod))
+    except Exception:
+        return False
+
+
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_pins_reject_mutant(name):
     mod = load_mutant(*MUTATIONS[name])
-    failed = [p.__name__ for p in PINS if not p(mod)]
+    failed = [p.__name__ for p in PINS if not passes(p, mod)]
     assert failed, f"no pin caught the mutation {name}"
