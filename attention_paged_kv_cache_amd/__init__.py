@@ -165,21 +165,43 @@ def _scale_ptr(x, device, keep):
 
 def batch_prefill_with_kv_cache(q, k_cache, v_cache, scale, workspace_buffer, *,
                                 max_token_per_sequence, max_sequence_kv,
-                                actual_seq_lens_q, actual_seq_lens_kv, block_tables,
+                                actual_seq_lens_q, actual_seq_lens_kv, block_tables=None,
                                 causal, return_lse=True, q_scale=None, k_scale=None,
-                                v_scale=None, out=None, lse=None, o_data_type=None,
+                                v_scale=None, batch_offsets_q=None, batch_offsets_o=None,
+                                batch_offsets_k=None, batch_offsets_v=None,
+                                batch_offsets_stats=None, out=None, lse=None, o_data_type=None,
                                 kv_layout="HND"):
-    """Batch prefill over a paged cache; returns (out, lse)."""
+    """Batch prefill; returns (out, lse).
+
+    With block_tables, k_cache / v_cache are paged ([pages, H, ps, d] for HND,
+    [pages, ps, H, d] for NHD). Without, they are [total_kv_rows, H_kv, d] and
+    request b's keys start at row batch_offsets_k[b] (values at
+    batch_offsets_v[b]). batch_offsets_q / _o / _stats give each request's
+    first row in q, out and lse. Absent offsets mean rows packed in request
+    order.
+    """
     if not return_lse:
         raise ValueError("return_lse must be True")
-    layout = _layout(kv_layout)
     dev = q.device
-    ps, hkv, d_qk = _cache_dims(k_cache, layout)
-    _, _, d_vo = _cache_dims(v_cache, layout)
-    for t in (k_cache, v_cache):
-        if t.dim() != 4 or t.stride(-1) != 1 or t.stride(-2) != t.shape[-1] or \
-                t.stride(1) != t.shape[2] * t.shape[3]:
-            raise ValueError("each page of k_cache/v_cache must be contiguous")
+    paged = block_tables is not None
+    if paged:
+        layout = _layout(kv_layout)
+        ps, hkv, d_qk = _cache_dims(k_cache, layout)
+        _, _, d_vo = _cache_dims(v_cache, layout)
+        for t in (k_cache, v_cache):
+            if t.dim() != 4 or t.stride(-1) != 1 or t.stride(-2) != t.shape[-1] or \
+                    t.stride(1) != t.shape[2] * t.shape[3]:
+                raise ValueError("each page of k_cache/v_cache must be contiguous")
+    else:
+        layout, ps = NHD, 16
+        for t in (k_cache, v_cache):
+            if t.dim() != 3 or not t.is_contiguous():
+                raise ValueError("without block_tables, k_cache/v_cache must be contiguous "
+                                 "[total_kv_rows, num_heads_kv, d]")
+        hkv, d_qk = k_cache.shape[1], k_cache.shape[2]
+        d_vo = v_cache.shape[2]
+        if v_cache.shape[1] != hkv:
+            raise ValueError("k_cache and v_cache must have the same number of heads")
     if q.dim() != 3 or q.shape[2] != d_qk:
         raise ValueError("q must be [total_tokens, num_heads_qo, d_qk]")
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
@@ -192,21 +214,32 @@ def batch_prefill_with_kv_cache(q, k_cache, v_cache, scale, workspace_buffer, *,
         out = torch.empty(q.shape[0], h_qo, d_vo, dtype=o_data_type, device=dev)
     if lse is None:
         lse = torch.empty(q.shape[0], h_qo, dtype=torch.float32, device=dev)
-    if out.dtype != o_data_type or not out.is_contiguous() or tuple(out.shape) != (q.shape[0], h_qo, d_vo):
-        raise ValueError("out must be a contiguous [total_tokens, num_heads_qo, d_vo] tensor")
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (q.shape[0], h_qo):
-        raise ValueError("lse must be a contiguous float32 [total_tokens, num_heads_qo] tensor")
+    if out.dtype != o_data_type or not out.is_contiguous() or out.dim() != 3 or \
+            tuple(out.shape[1:]) != (h_qo, d_vo):
+        raise ValueError("out must be a contiguous [rows, num_heads_qo, d_vo] tensor")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.dim() != 2 or \
+            lse.shape[1] != h_qo:
+        raise ValueError("lse must be a contiguous float32 [rows, num_heads_qo] tensor")
     lq = _i32_on(actual_seq_lens_q, dev)
     lkv = _i32_on(actual_seq_lens_kv, dev)
-    bt = _i32_on(block_tables, dev)
+    bt = _i32_on(block_tables, dev) if paged else None
+    offs = [None if x is None else _i32_on(x, dev) for x in
+            (batch_offsets_q, batch_offsets_o, batch_offsets_k, batch_offsets_v,
+             batch_offsets_stats)]
+    for o in offs:
+        if o is not None and o.shape[0] != lq.shape[0]:
+            raise ValueError("batch offsets must have batch_size entries")
     keep = []
     _lib.check(_lib.load().pkv_batch_prefill_with_kv_cache(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), k_cache.stride(0), v_cache.stride(0),
-        float(scale), _ptr(workspace_buffer), workspace_buffer.numel() * workspace_buffer.element_size(),
-        int(max_token_per_sequence), int(max_sequence_kv), _ptr(lq), _ptr(lkv), _ptr(bt),
-        bt.shape[1], lq.shape[0], h_qo, hkv, d_qk, d_vo, ps, layout, 1 if causal else 0,
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), k_cache.stride(0) if paged else 0,
+        v_cache.stride(0) if paged else 0, float(scale), _ptr(workspace_buffer),
+        workspace_buffer.numel() * workspace_buffer.element_size(),
+        int(max_token_per_sequence), int(max_sequence_kv), _ptr(lq), _ptr(lkv),
+        _ptr(bt) if paged else None, bt.shape[1] if paged else 0, lq.shape[0], h_qo, hkv,
+        d_qk, d_vo, ps, layout, 1 if causal else 0,
         _scale_ptr(q_scale, dev, keep), _scale_ptr(k_scale, dev, keep),
-        _scale_ptr(v_scale, dev, keep), _ptr(out), _ptr(lse), _dt(q), _dt(out), _stream()),
+        _scale_ptr(v_scale, dev, keep), _ptr(out), _ptr(lse), _dt(q), _dt(out),
+        *[None if o is None else _ptr(o) for o in offs], _stream()),
         "batch_prefill_with_kv_cache")
     return out, lse
 

@@ -43,7 +43,7 @@ SIGNATURES = {
     "pkv_batch_prefill_with_kv_cache": (ctypes.c_int, [
         _P, _P, _P, _I64, _I64, _F, _P, _SZ, _I32, _I32, _P, _P, _P, _I32, _I32,
         _I32, _I32, _I32, _I32, _I32, ctypes.c_int, _I32, _P, _P, _P, _P, _P,
-        ctypes.c_int, ctypes.c_int, _P]),
+        ctypes.c_int, ctypes.c_int, _P, _P, _P, _P, _P, _P]),
     "pkv_decode_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_batch_decode_with_kv_cache": (ctypes.c_int, [
         _P, _P, _P, _I64, _I64, _P, _SZ, _P, _I32, _P, _I32, _I32, _F, _F, _I32,

@@ -157,9 +157,15 @@ PKV_API pkv_status pkv_append_paged_kv_cache(
   return from_hip(pkv::launch_append(a, as_stream(stream)), __func__);
 }
 
+// Two 256-byte-aligned regions of batch_size + 1 int32: the query-row and
+// key-row prefix sums used when offsets are not given.
+static size_t prefill_region_bytes(int32_t batch_size) {
+  return ((size_t)(batch_size + 1) * sizeof(int32_t) + 255) / 256 * 256;
+}
+
 PKV_API size_t pkv_prefill_workspace_size(int32_t batch_size) {
   if (batch_size < 0) return 0;
-  return ((size_t)(batch_size + 1) * sizeof(int32_t) + 255) / 256 * 256;
+  return 2 * prefill_region_bytes(batch_size);
 }
 
 PKV_API pkv_status pkv_batch_prefill_with_kv_cache(
@@ -172,8 +178,13 @@ PKV_API pkv_status pkv_batch_prefill_with_kv_cache(
     int32_t num_heads_kv, int32_t d_qk, int32_t d_vo, int32_t page_size,
     pkv_layout kv_layout, int32_t causal, const float *q_scale,
     const float *k_scale, const float *v_scale, void *out, float *lse,
-    pkv_dtype qkv_dtype, pkv_dtype o_dtype, void *stream) {
+    pkv_dtype qkv_dtype, pkv_dtype o_dtype, const int32_t *batch_offsets_q,
+    const int32_t *batch_offsets_o, const int32_t *batch_offsets_k,
+    const int32_t *batch_offsets_v, const int32_t *batch_offsets_stats, void *stream) {
+  const bool paged = block_tables != nullptr;
   CHECK(batch_size >= 0, PKV_ERR_INVALID_ARG, "batch_size < 0");
+  CHECK(!paged || (batch_offsets_k == nullptr && batch_offsets_v == nullptr),
+        PKV_ERR_INVALID_ARG, "batch_offsets_k / batch_offsets_v apply only without block_tables");
   CHECK(num_heads_kv > 0 && num_heads_qo > 0, PKV_ERR_INVALID_ARG,
         "head counts must be positive");
   CHECK(num_heads_qo >= num_heads_kv, PKV_ERR_INVALID_ARG,
@@ -189,28 +200,30 @@ PKV_API pkv_status pkv_batch_prefill_with_kv_cache(
         PKV_ERR_INVALID_ARG, "unknown q/k/v dtype");
   CHECK(o_dtype == PKV_F16 || o_dtype == PKV_BF16, PKV_ERR_UNSUPPORTED,
         "output dtype must be F16 or BF16");
-  CHECK(page_size_ok(page_size), PKV_ERR_UNSUPPORTED,
-        "page_size must be 16, 32 or 64");
   CHECK(max_token_per_sequence >= 0 && max_sequence_kv >= 0,
         PKV_ERR_INVALID_ARG, "negative maximum length");
-  CHECK(max_pages_per_seq > 0, PKV_ERR_INVALID_ARG, "max_pages_per_seq <= 0");
-  CHECK((int64_t)max_pages_per_seq * page_size >= max_sequence_kv,
-        PKV_ERR_INVALID_ARG, "block_tables too narrow for max_sequence_kv");
   CHECK(lse != nullptr, PKV_ERR_INVALID_ARG,
         "lse is required (the log-sum-exp must be returned)");
   const int es = elem_bytes(qkv_dtype);
-  const int64_t pk = (int64_t)page_size * num_heads_kv * d_qk;
-  const int64_t pv = (int64_t)page_size * num_heads_kv * d_vo;
-  CHECK(page_stride_k >= pk && page_stride_v >= pv, PKV_ERR_INVALID_ARG,
-        "page stride smaller than one page");
-  CHECK((page_stride_k * es) % 16 == 0 && (page_stride_v * es) % 16 == 0,
-        PKV_ERR_UNSUPPORTED, "page strides must be multiples of 16 bytes");
+  if (paged) {
+    CHECK(page_size_ok(page_size), PKV_ERR_UNSUPPORTED,
+          "page_size must be 16, 32 or 64");
+    CHECK(max_pages_per_seq > 0, PKV_ERR_INVALID_ARG, "max_pages_per_seq <= 0");
+    CHECK((int64_t)max_pages_per_seq * page_size >= max_sequence_kv,
+          PKV_ERR_INVALID_ARG, "block_tables too narrow for max_sequence_kv");
+    const int64_t pk = (int64_t)page_size * num_heads_kv * d_qk;
+    const int64_t pv = (int64_t)page_size * num_heads_kv * d_vo;
+    CHECK(page_stride_k >= pk && page_stride_v >= pv, PKV_ERR_INVALID_ARG,
+          "page stride smaller than one page");
+    CHECK((page_stride_k * es) % 16 == 0 && (page_stride_v * es) % 16 == 0,
+          PKV_ERR_UNSUPPORTED, "page strides must be multiples of 16 bytes");
+  }
   CHECK(workspace_bytes >= pkv_prefill_workspace_size(batch_size),
         PKV_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than "
         "pkv_prefill_workspace_size(batch_size)");
   if (batch_size == 0 || max_token_per_sequence == 0) return PKV_OK;
   CHECK(q && k_cache && v_cache && workspace && actual_seq_lens_q &&
-            actual_seq_lens_kv && block_tables && out,
+            actual_seq_lens_kv && out,
         PKV_ERR_INVALID_ARG, "null pointer");
   CHECK(aligned(q, 16) && aligned(k_cache, 16) && aligned(v_cache, 16) &&
             aligned(out, 16) && aligned(workspace, 16),
@@ -222,7 +235,7 @@ PKV_API pkv_status pkv_batch_prefill_with_kv_cache(
   a.v = v_cache;
   a.page_stride_k = page_stride_k;
   a.page_stride_v = page_stride_v;
-  if (kv_layout == PKV_NHD) {
+  if (kv_layout == PKV_NHD || !paged) {  // unpaged rows are [row][head][d]
     a.slot_stride_k = (int64_t)num_heads_kv * d_qk;
     a.head_stride_k = d_qk;
     a.slot_stride_v = (int64_t)num_heads_kv * d_vo;
@@ -235,15 +248,22 @@ PKV_API pkv_status pkv_batch_prefill_with_kv_cache(
   }
   a.lens_q = actual_seq_lens_q;
   a.lens_kv = actual_seq_lens_kv;
-  a.cum_q = reinterpret_cast<int32_t *>(workspace);
+  int32_t *cum_q = reinterpret_cast<int32_t *>(workspace);
+  int32_t *cum_kv = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(workspace) +
+                                                prefill_region_bytes(batch_size));
+  a.off_q = batch_offsets_q ? batch_offsets_q : cum_q;
+  a.off_o = batch_offsets_o ? batch_offsets_o : cum_q;
+  a.off_lse = batch_offsets_stats ? batch_offsets_stats : cum_q;
   a.block_tables = block_tables;
+  a.off_k = batch_offsets_k ? batch_offsets_k : cum_kv;
+  a.off_v = batch_offsets_v ? batch_offsets_v : cum_kv;
   a.max_pages = max_pages_per_seq;
   a.batch = batch_size;
   a.num_heads_qo = num_heads_qo;
   a.num_heads_kv = num_heads_kv;
   a.d_qk = d_qk;
   a.d_vo = d_vo;
-  a.page_size = page_size;
+  a.page_size = paged ? page_size : 16;  // unpaged: 16-row groups per wave
   a.max_q = max_token_per_sequence;
   a.causal = causal ? 1 : 0;
   a.scale = scale;
@@ -255,9 +275,15 @@ PKV_API pkv_status pkv_batch_prefill_with_kv_cache(
   a.qkv_dtype = qkv_dtype;
   a.o_dtype = o_dtype;
   hipStream_t s = as_stream(stream);
-  hipError_t e = pkv::launch_exclusive_cumsum(
-      actual_seq_lens_q, batch_size, reinterpret_cast<int32_t *>(workspace), s);
-  if (e != hipSuccess) return from_hip(e, __func__);
+  if (!batch_offsets_q || !batch_offsets_o || !batch_offsets_stats) {
+    const hipError_t e = pkv::launch_exclusive_cumsum(actual_seq_lens_q, batch_size, cum_q, s);
+    if (e != hipSuccess) return from_hip(e, __func__);
+  }
+  if (!paged && (!batch_offsets_k || !batch_offsets_v)) {
+    const hipError_t e =
+        pkv::launch_exclusive_cumsum(actual_seq_lens_kv, batch_size, cum_kv, s);
+    if (e != hipSuccess) return from_hip(e, __func__);
+  }
   return from_hip(pkv::launch_prefill(a, s), __func__);
 }
 

@@ -45,8 +45,13 @@ struct PrefillArgs {
   int64_t page_stride_k, page_stride_v;  // elements
   int64_t slot_stride_k, head_stride_k;  // elements
   int64_t slot_stride_v, head_stride_v;  // elements
-  const int32_t *lens_q, *lens_kv, *cum_q;
+  const int32_t *lens_q, *lens_kv;
+  // first row of each request in q, out and lse ([batch] int32 each)
+  const int32_t *off_q, *off_o, *off_lse;
+  // null: K/V are not paged; request b's key / value rows start at row
+  // off_k[b] / off_v[b] of [rows, H_kv, d] tensors
   const int32_t *block_tables;
+  const int32_t *off_k, *off_v;
   int32_t max_pages;
   int32_t batch, num_heads_qo, num_heads_kv, d_qk, d_vo, page_size;
   int32_t max_q;

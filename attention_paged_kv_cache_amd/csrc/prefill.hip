@@ -161,7 +161,7 @@ __device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, int voff, char 
 // Wait until this wave's outstanding global loads (LDS DMA included) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <class ET, int DQK, class OT>
+template <class ET, int DQK, class OT, bool PAGED>
 __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void prefill_kernel(
     PrefillArgs a, int32_t T, int32_t Gc, int32_t head_chunks,
     int32_t n_qtiles) {
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   // ---- Q^T operand in registers -------------------------------------------
   u32x4 qreg[G_::NQ];
   {
-    const int64_t qrow = (int64_t)(a.cum_q[b] + tok) * a.num_heads_qo + head;
+    const int64_t qrow = (int64_t)(a.off_q[b] + tok) * a.num_heads_qo + head;
     const char *qp = (const char *)a.q + qrow * G_::ROWB;
     const uint32_t flip = negate ? (ES == 1 ? 0x80808080u : 0x80008000u) : 0u;
 #pragma unroll
@@ -266,7 +266,14 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   // (page sizes 16, 32, 64). The page index is clamped into the sequence so
   // that padding entries of the block table are never followed.
   const int r0 = 16 * wave;
-  auto wave_page = [&](int j) { return bt[min((j * kKeys + r0) >> log2ps, last_pg)]; };
+  auto wave_page = [&](int j) {
+    if constexpr (PAGED) return bt[min((j * kKeys + r0) >> log2ps, last_pg)];
+    else return 0;  // rows are addressed directly (dma_prep)
+  };
+  // Without paging each wave's 16 keys are 16 consecutive rows from
+  // off_k[b] + key (off_v[b] + key for values).
+  const int row_k = PAGED ? 0 : a.off_k[b];
+  const int row_v = PAGED ? 0 : a.off_v[b];
 
   // Per-lane source rows / columns of each 1 KB LDS DMA of this wave's 16 K
   // rows (a whole number of KB per wave: lanes that fall in the row padding
@@ -301,10 +308,17 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   auto dma_prep = [&](int j, int page, char *stage) {
     Dma d;
     const int key0 = j * kKeys + r0;
-    d.rk = make_rsrc(kbase + (int64_t)page * psk, page_bytes_k);
-    d.rv = make_rsrc(vbase + (int64_t)page * psv, page_bytes_v);
     const bool in = key0 <= L_kv - 1;
-    d.slot0 = in ? (key0 & ps_mask) : ((L_kv - 1) & ps_mask);
+    if constexpr (PAGED) {
+      d.rk = make_rsrc(kbase + (int64_t)page * psk, page_bytes_k);
+      d.rv = make_rsrc(vbase + (int64_t)page * psv, page_bytes_v);
+      d.slot0 = in ? (key0 & ps_mask) : ((L_kv - 1) & ps_mask);
+    } else {
+      const int key = in ? key0 : L_kv - 1;
+      d.rk = make_rsrc(kbase + (int64_t)(row_k + key) * ssk, (int)(15 * ssk + G_::ROWB));
+      d.rv = make_rsrc(vbase + (int64_t)(row_v + key) * ssv, (int)(15 * ssv + G_::VRB));
+      d.slot0 = 0;
+    }
     d.lim_row = in ? (L_kv - 1 - key0) : 0;
     d.kl = stage + wave * G_::WKB;
     d.vl = stage + G_::K_BYTES + r0 * G_::VRB;
@@ -495,7 +509,7 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   const float l_tot = wave_sum_xor32(l_run);
   if (!row_ok) return;
   const float inv = l_tot > 0.0f ? vs / l_tot : 0.0f;
-  const int64_t orow = (int64_t)(a.cum_q[b] + tok) * a.num_heads_qo + head;
+  const int64_t orow = (int64_t)(a.off_o[b] + tok) * a.num_heads_qo + head;
   char *op = (char *)a.out + orow * kDvo * 2;
 #pragma unroll
   for (int md = 0; md < 4; ++md)
@@ -508,7 +522,8 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
       st8(op + d * 2, w);
     }
   if (half == 0)
-    a.lse[orow] = l_tot > 0.0f ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
+    a.lse[(int64_t)(a.off_lse[b] + tok) * a.num_heads_qo + head] =
+        l_tot > 0.0f ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
 }
 
 template <class ET, int DQK, class OT>
@@ -523,9 +538,12 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t s) {
   const int64_t blocks = (int64_t)kXcds * ((n_pairs + kXcds - 1) / kXcds) * n_qtiles;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_kernel<ET, DQK, OT>), dim3((uint32_t)blocks),
-                     dim3(kThreads), 0, s, a, T, Gc, head_chunks,
-                     n_qtiles);
+  if (a.block_tables)
+    hipLaunchKernelGGL((prefill_kernel<ET, DQK, OT, true>), dim3((uint32_t)blocks),
+                       dim3(kThreads), 0, s, a, T, Gc, head_chunks, n_qtiles);
+  else
+    hipLaunchKernelGGL((prefill_kernel<ET, DQK, OT, false>), dim3((uint32_t)blocks),
+                       dim3(kThreads), 0, s, a, T, Gc, head_chunks, n_qtiles);
   return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 
 typedef enum {
   PKV_OK = 0,
@@ -152,6 +152,15 @@ size_t pkv_prefill_workspace_size(int32_t batch_size);
  * bottom-right: query t sees keys j <= t + L_kv - L_q. Token j of request b
  * is slot j % page_size of page block_tables[b * max_pages_per_seq +
  * j / page_size].
+ * Without paging (block_tables NULL; the page's non-paged k_cache / v_cache
+ * of shape (total KV length, H_kv, d)), token j of request b is row
+ * batch_offsets_k[b] + j of k_cache and batch_offsets_v[b] + j of v_cache;
+ * page_size, page strides, max_pages_per_seq and kv_layout are then ignored.
+ * batch_offsets_q / _o / _k / _v / _stats ([batch_size] int32 on the device,
+ * the page's batch offsets, counted in rows) give the first row of each
+ * request in q, out, k_cache, v_cache and lse; each may be NULL, meaning the
+ * exclusive prefix sum of the request lengths (rows packed in request order).
+ * _k and _v apply only without paging (PKV_ERR_INVALID_ARG otherwise).
  *   q    [sum L_q, num_heads_qo, d_qk] contiguous, qkv_dtype; request b's
  *        rows start at the exclusive prefix sum of actual_seq_lens_q
  *   out  [sum L_q, num_heads_qo, d_vo], o_dtype (PKV_F16 or PKV_BF16)
@@ -177,7 +186,9 @@ pkv_status pkv_batch_prefill_with_kv_cache(
     int32_t num_heads_kv, int32_t d_qk, int32_t d_vo, int32_t page_size,
     pkv_layout kv_layout, int32_t causal, const float *q_scale,
     const float *k_scale, const float *v_scale, void *out, float *lse,
-    pkv_dtype qkv_dtype, pkv_dtype o_dtype, void *stream);
+    pkv_dtype qkv_dtype, pkv_dtype o_dtype, const int32_t *batch_offsets_q,
+    const int32_t *batch_offsets_o, const int32_t *batch_offsets_k,
+    const int32_t *batch_offsets_v, const int32_t *batch_offsets_stats, void *stream);
 
 /* Workspace bytes pkv_batch_decode_with_kv_cache needs for these sizes. */
 size_t pkv_decode_workspace_size(int32_t batch_size, int32_t q_len_per_req,

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.pkv_abi_version() == 2
+    assert lib.pkv_abi_version() == 3
 
 
 def _err(lib):
@@ -52,7 +52,7 @@ def _prefill(lib, **over):
              ws=FAKE, ws_bytes=4096, max_q=10, max_kv=10, lq=FAKE, lkv=FAKE, bt=FAKE,
              max_pages=1, batch=1, hqo=32, hkv=8, dqk=128, dvo=128, ps=16, layout=1,
              causal=1, qs=None, ks=None, vs=None, out=FAKE, lse=FAKE, qdt=1, odt=1,
-             stream=None)
+             off_q=None, off_o=None, off_k=None, off_v=None, off_stats=None, stream=None)
     a.update(over)
     return lib.pkv_batch_prefill_with_kv_cache(*a.values())
 
@@ -70,6 +70,10 @@ def _prefill(lib, **over):
     (dict(batch=-1), "batch_size"),
     (dict(psk=100), "page stride"),
     (dict(max_kv=17), "too narrow"),
+    (dict(off_k=FAKE), "only without block_tables"),
+    (dict(off_v=FAKE), "only without block_tables"),
+    (dict(bt=None, qdt=7), "dtype"),
+    (dict(bt=None, dqk=64), "128 or 192"),
 ])
 def test_prefill_validation(lib, over, needle):
     st = _prefill(lib, **over)
