@@ -135,6 +135,12 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
   // each row's draft mask as bits (bit i: draft i visible), when a mask is
   // given; read only on the steps that reach the drafts
   __shared__ uint64_t sh_mbits[R];
+  // With 48 or 64 rows the Q^T operands (16 VGPRs per 16-row block) stay in
+  // LDS, one 16-byte slot per (block, k-step, lane), and are read back each
+  // step: that leaves room for the accumulators and two steps of K/V loads
+  // without spilling. Fewer rows keep them in registers.
+  constexpr bool kQInLds = NB >= 3;
+  __shared__ u32x4 sh_q[kQInLds ? NB : 1][4][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -172,7 +178,7 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
   const float c = fmaxf(fabsf(c_raw), 1e-30f);
 
   // ---- Q^T operands: row n = 16*nb + r16 -> (query qi, head g) ------------
-  u32x4 qop[NB][4];
+  u32x4 qop[kQInLds ? 1 : NB][4];
   int pos[NB], wlo[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -192,9 +198,14 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
       u32x4 v = {0u, 0u, 0u, 0u};
       if (ok) v = ld16(qp + kstep_d<FP8>(s, g4) * 2);
       v[0] ^= flip; v[1] ^= flip; v[2] ^= flip; v[3] ^= flip;
-      qop[nb][s] = v;
+      if constexpr (kQInLds) {
+        if (wave == 0) sh_q[nb][s][lane] = v;  // every wave holds the same values
+      } else {
+        qop[nb][s] = v;
+      }
     }
   }
+  if constexpr (kQInLds) __syncthreads();
   if (a.mask) {  // uniform: every thread takes the barrier or none does
     if (tid < R) {
       uint64_t bits = 0;
@@ -314,7 +325,19 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
       for (int nb = 0; nb < NB; ++nb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma16(kop[mb][s], qop[nb][s], acc, QT{});
+        for (int s = 0; s < 4; ++s) {
+          if constexpr (kQInLds) {
+            // the empty asm hides the slot address, so the reads are not
+            // hoisted out of the key loop back into registers
+            int qaddr = ((nb * 4 + s) * 64 + lane) * 16;
+            asm volatile("" : "+v"(qaddr));
+            const u32x4 q = *reinterpret_cast<const u32x4 *>(
+                reinterpret_cast<const char *>(&sh_q[0][0][0]) + qaddr);
+            acc = mfma16(kop[mb][s], q, acc, QT{});
+          } else {
+            acc = mfma16(kop[mb][s], qop[nb][s], acc, QT{});
+          }
+        }
         sacc[mb][nb] = acc;
       }
 
