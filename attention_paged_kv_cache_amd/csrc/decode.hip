@@ -42,6 +42,7 @@ namespace pkv {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kXcds = 8;  // workgroups are dispatched round-robin over 8 XCDs
 constexpr int kWaves = 4;
 constexpr int kD = 128;
 
@@ -122,11 +123,13 @@ __device__ __forceinline__ int kstep_d(int t, int g4) {
   return FP8 ? 64 * (t >> 1) + 16 * g4 + 8 * (t & 1) : 32 * t + 8 * g4;
 }
 
-// NB: number of 16-row blocks of the (q_len x G) query rows of a kv head.
+// NB: number of 16-row blocks a workgroup takes of the (q_len x G) query
+// rows of a kv head (1 or 2). More than 32 rows are split into n_groups
+// groups of 32, one workgroup each.
 template <int NB, class QT, bool FP8>
-__global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) void decode_kernel(
-    DecodeArgs a, int32_t chunk, int32_t max_splits, float *__restrict__ ws_o,
-    float *__restrict__ ws_ml) {
+__global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_kernel(
+    DecodeArgs a, int32_t chunk, int32_t max_splits, int32_t n_groups,
+    float *__restrict__ ws_o, float *__restrict__ ws_ml) {
   constexpr int ES = FP8 ? 1 : 2;
   constexpr int R = NB * 16;
   __shared__ float sh_m[kWaves][R];
@@ -135,12 +138,6 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
   // each row's draft mask as bits (bit i: draft i visible), when a mask is
   // given; read only on the steps that reach the drafts
   __shared__ uint64_t sh_mbits[R];
-  // With 48 or 64 rows the Q^T operands (16 VGPRs per 16-row block) stay in
-  // LDS, one 16-byte slot per (block, k-step, lane), and are read back each
-  // step: that leaves room for the accumulators and two steps of K/V loads
-  // without spilling. Fewer rows keep them in registers.
-  constexpr bool kQInLds = NB >= 3;
-  __shared__ u32x4 sh_q[kQInLds ? NB : 1][4][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -148,14 +145,27 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
   const int g4 = lane >> 4;
   const int r16 = lane & 15;
 
+  // Block -> (unit u = (split, request, kv head), row group). The row groups
+  // of one unit sit 8 blocks apart, so they run on the same XCD, close in
+  // time, and the second streams the unit's K/V from that XCD's L2.
   const int bh = a.batch * a.num_heads_kv;
-  const int split = blockIdx.x / bh;
-  const int b = (blockIdx.x / a.num_heads_kv) % a.batch;
-  const int kvh = blockIdx.x % a.num_heads_kv;
+  int u = blockIdx.x, grp = 0;
+  if (n_groups > 1) {
+    const int rest = blockIdx.x / kXcds;
+    grp = rest % n_groups;
+    u = (rest / n_groups) * kXcds + blockIdx.x % kXcds;
+    if (u >= bh * max_splits) return;
+  }
+  const int split = u / bh;
+  const int b = (u / a.num_heads_kv) % a.batch;
+  const int kvh = u % a.num_heads_kv;
   const int seq = (int)a.seq_lens[b];
   int ql, qrow0;
   request_rows(a, b, ql, qrow0);
-  if (ql <= 0) return;
+  const int G = a.num_heads_qo / a.num_heads_kv;
+  const int row_base = grp * R;                // this group's first row
+  const int rows = min(R, ql * G - row_base);  // its rows of this request
+  if (rows <= 0) return;
   const int lo = key_origin(a, seq, ql);
   const int k_begin = lo + split * chunk;
   if (k_begin >= seq) return;
@@ -165,9 +175,7 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
   const int w_begin = k_begin + wave * cw;
   const int w_end = min(k_end, w_begin + cw);
 
-  const int G = a.num_heads_qo / a.num_heads_kv;
-  const int rows = ql * G;            // this request's rows
-  const int rows_ws = a.q_len * G;    // workspace rows per unit (the maximum)
+  const int rows_ws = a.q_len * G;  // workspace rows per unit (the maximum)
   // With a draft mask, keys from the first draft on are allowed by the
   // mask; keys before it only by the window.
   const int dstart = seq - ql;
@@ -178,12 +186,13 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
   const float c = fmaxf(fabsf(c_raw), 1e-30f);
 
   // ---- Q^T operands: row n = 16*nb + r16 -> (query qi, head g) ------------
-  u32x4 qop[kQInLds ? 1 : NB][4];
+  u32x4 qop[NB][4];
   int pos[NB], wlo[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int n = nb * 16 + r16;
-    const int qi = n / G, g = n - qi * G;
+    const int ng = row_base + n;
+    const int qi = ng / G, g = ng - qi * G;
     const bool ok = n < rows;
     const int qpos = seq - ql + qi;  // the query's position
     // last allowed key (padding rows: none); with a mask every key up to
@@ -198,19 +207,14 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
       u32x4 v = {0u, 0u, 0u, 0u};
       if (ok) v = ld16(qp + kstep_d<FP8>(s, g4) * 2);
       v[0] ^= flip; v[1] ^= flip; v[2] ^= flip; v[3] ^= flip;
-      if constexpr (kQInLds) {
-        if (wave == 0) sh_q[nb][s][lane] = v;  // every wave holds the same values
-      } else {
-        qop[nb][s] = v;
-      }
+      qop[nb][s] = v;
     }
   }
-  if constexpr (kQInLds) __syncthreads();
   if (a.mask) {  // uniform: every thread takes the barrier or none does
     if (tid < R) {
       uint64_t bits = 0;
-      if (tid < rows) {  // ql <= 64 because rows = ql * G <= 64
-        const uint8_t *mrow = a.mask + ((int64_t)b * a.q_len + tid / G) * a.q_len;
+      if (tid < rows) {  // ql <= 64 because ql * G <= 64
+        const uint8_t *mrow = a.mask + ((int64_t)b * a.q_len + (row_base + tid) / G) * a.q_len;
         for (int i = 0; i < ql; ++i)
           if (mrow[i]) bits |= 1ull << i;
       }
@@ -325,19 +329,7 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
       for (int nb = 0; nb < NB; ++nb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if constexpr (kQInLds) {
-            // the empty asm hides the slot address, so the reads are not
-            // hoisted out of the key loop back into registers
-            int qaddr = ((nb * 4 + s) * 64 + lane) * 16;
-            asm volatile("" : "+v"(qaddr));
-            const u32x4 q = *reinterpret_cast<const u32x4 *>(
-                reinterpret_cast<const char *>(&sh_q[0][0][0]) + qaddr);
-            acc = mfma16(kop[mb][s], q, acc, QT{});
-          } else {
-            acc = mfma16(kop[mb][s], qop[nb][s], acc, QT{});
-          }
-        }
+        for (int s = 0; s < 4; ++s) acc = mfma16(kop[mb][s], qop[nb][s], acc, QT{});
         sacc[mb][nb] = acc;
       }
 
@@ -488,8 +480,9 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
     float L = 0.0f;
     for (int w = 0; w < kWaves; ++w) L += sh_l[w][n] * fast_exp2(sh_m[w][n] - M_use);
     const float *src = &sh_o[n][d4];
+    const int ng = row_base + n;
     if (direct) {
-      const int qi = n / G, g = n - qi * G;
+      const int qi = ng / G, g = ng - qi * G;
       const int head = kvh * G + g;
       float den = L;
       if (a.sinks) den += fast_exp2(a.sinks[head] * kLog2e - M_use);
@@ -516,11 +509,11 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || (NB == 2 && FP8)) ? 2 : 1) vo
       }
     } else {
       const int64_t unit = ((int64_t)b * a.num_heads_kv + kvh) * max_splits + split;
-      float *dst = ws_o + (unit * rows_ws + n) * kD + d4;
+      float *dst = ws_o + (unit * rows_ws + ng) * kD + d4;
       *reinterpret_cast<f32x4 *>(dst) = f32x4{src[0], src[1], src[2], src[3]};
       if (d4 == 0) {
-        ws_ml[(unit * rows_ws + n) * 2 + 0] = M;
-        ws_ml[(unit * rows_ws + n) * 2 + 1] = L;
+        ws_ml[(unit * rows_ws + ng) * 2 + 0] = M;
+        ws_ml[(unit * rows_ws + ng) * 2 + 1] = L;
       }
     }
   }
@@ -586,10 +579,16 @@ hipError_t launch_nb(const DecodeArgs &a, const DecodePlan &p, hipStream_t s) {
   const int64_t units = (int64_t)a.batch * a.num_heads_kv;
   float *ws_o = ws;
   float *ws_ml = ws + units * p.max_splits * p.rows * kD;
-  const int64_t blocks = units * p.max_splits;
-  if (blocks == 0) return hipSuccess;
+  const int64_t n_units = units * p.max_splits;
+  if (n_units == 0) return hipSuccess;
+  // rows beyond 32 per kv head: groups of 32, each unit's groups on one XCD
+  const int n_groups = (p.rows + 31) / 32;
+  const int64_t blocks =
+      n_groups == 1 ? n_units : (n_units + kXcds - 1) / kXcds * kXcds * n_groups;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((decode_kernel<NB, QT, FP8>), dim3((uint32_t)blocks),
-                     dim3(kThreads), 0, s, a, p.chunk, p.max_splits, ws_o, ws_ml);
+                     dim3(kThreads), 0, s, a, p.chunk, p.max_splits, n_groups, ws_o,
+                     ws_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.max_splits == 1) return e;
   const int64_t waves = units * p.rows;
@@ -600,12 +599,9 @@ hipError_t launch_nb(const DecodeArgs &a, const DecodePlan &p, hipStream_t s) {
 
 template <class QT, bool FP8>
 hipError_t launch_q(const DecodeArgs &a, const DecodePlan &p, hipStream_t s) {
-  switch ((p.rows + 15) / 16) {
-    case 1: return launch_nb<1, QT, FP8>(a, p, s);
-    case 2: return launch_nb<2, QT, FP8>(a, p, s);
-    case 3: return launch_nb<3, QT, FP8>(a, p, s);
-    default: return launch_nb<4, QT, FP8>(a, p, s);
-  }
+  // up to 16 rows: one 16-row block; more: 32-row workgroups
+  if (p.rows <= 16) return launch_nb<1, QT, FP8>(a, p, s);
+  return launch_nb<2, QT, FP8>(a, p, s);
 }
 
 }  // namespace

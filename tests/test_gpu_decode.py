@@ -423,3 +423,33 @@ def test_spec_mask_with_variable_length_queries(pkv):
     n = int(cum[-1])
     ref = oracle_decode_ragged(w, cum, mask)
     assert_out_close(got[:n], ref, got.dtype)
+
+
+@pytest.mark.parametrize("ql,hqo,seq,window,seed", [
+    (3, 16, (3000, 12000), 5000, 120),   # 48 rows: a full and a half group, split KV
+    (4, 16, (1, 900), -1, 121),          # 64 rows: two full groups, one split
+    (2, 24, (2000, 9000), -1, 122),      # 48 rows with GQA 24
+])
+def test_row_groups(pkv, ql, hqo, seq, window, seed):
+    # more than 32 rows per kv head run as groups of 32 rows, one workgroup each
+    hkv = 1 if hqo == 16 else 2
+    check(pkv, small(seed=seed, seq=seq, batch=4, q_len_per_req=ql, num_qo_heads=hqo,
+                     num_kv_heads=hkv, window_left=window, sinks=True))
+
+
+def test_row_groups_with_ragged_queries_and_mask(pkv):
+    # 4 x 16 = 64 rows at most: ragged counts leave the second group partial
+    # or empty; the draft mask spans both groups
+    q_max = 4
+    w = small(seed=123, seq=(500, 7000), batch=6, q_len_per_req=q_max, window_left=900,
+              sinks=True, num_qo_heads=16, num_kv_heads=1, kv_dtype=torch.float8_e4m3fn,
+              page_size=32)
+    rng = np.random.default_rng(123)
+    counts = np.array([4, 1, 2, 0, 3, 4])
+    cum = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    mask = torch.from_numpy(_tree_mask(6, q_max, rng)).to(DEV)
+    out = torch.full_like(w["query"], float("nan"))
+    got = run_ragged(pkv, w, cum, q_max, mask=mask, out=out)
+    n = int(cum[-1])
+    assert_out_close(got[:n], oracle_decode_ragged(w, cum, mask), got.dtype)
+    assert torch.isnan(got[n:].float()).all()
