@@ -453,3 +453,17 @@ def test_row_groups_with_ragged_queries_and_mask(pkv):
     n = int(cum[-1])
     assert_out_close(got[:n], oracle_decode_ragged(w, cum, mask), got.dtype)
     assert torch.isnan(got[n:].float()).all()
+
+
+def test_full_size_spec_decode_mask_and_offsets_reproduce_causal(pkv):
+    # the speculative-decoding workload: a lower-triangular draft mask and
+    # explicit uniform query offsets each reproduce the implicit causal
+    # decode bitwise
+    w = workloads.spec_decode(DEV)
+    a = run_decode(pkv, w)
+    tril = torch.ones(64, 4, 4, dtype=torch.bool).tril().to(DEV)
+    b = run_ragged(pkv, w, None, 4, mask=tril)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    cum = (np.arange(65) * 4).astype(np.int32)
+    c = run_ragged(pkv, w, cum, 4)
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))

@@ -136,3 +136,16 @@ def test_offsets_reorder_with_gaps_against_oracle(pkv, fp8):
     # rows no request owns are never written
     assert torch.isnan(out[torch.from_numpy(~written_o).to(DEV)].float()).all()
     assert torch.isnan(lse[torch.from_numpy(~written_l).to(DEV)]).all()
+
+
+def test_full_size_unpaged_equals_paged_bitwise(pkv):
+    # the benchmark's prefill workload (batch 16, 65536-page pool), gathered
+    # into packed rows
+    w = workloads.batch_prefill(DEV)
+    out_p, lse_p = run_prefill(pkv, w)
+    bt = w["block_tables"]
+    k = contiguous_rows(w["k_cache"], bt, w["seq_lens_kv"], w["layout"])
+    v = contiguous_rows(w["v_cache"], bt, w["seq_lens_kv"], w["layout"])
+    out_u, lse_u = unpaged_call(pkv, w, k, v)
+    assert torch.equal(out_p.view(torch.int16), out_u.view(torch.int16))
+    assert torch.equal(lse_p.view(torch.int32), lse_u.view(torch.int32))
