@@ -49,7 +49,8 @@ def assert_lse_close(got, ref, atol=1e-3):
     got = got.detach().cpu().numpy().astype(np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     both_inf = np.isneginf(got) & np.isneginf(ref)
-    err = np.where(both_inf, 0.0, np.abs(got - ref))
+    with np.errstate(invalid="ignore"):  # -inf - -inf where both rows are empty
+        err = np.where(both_inf, 0.0, np.abs(got - ref))
     assert not np.isnan(err).any(), "lse: NaN"
     assert err.max() <= atol, f"lse max err {err.max():.4g}"
     return float(err.max())
