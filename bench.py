@@ -13,7 +13,7 @@ measurements, each against the MI355X roofline, and the float64 oracle timed
 on the host for comparison.
 
 Rates come from warm back-to-back calls; each leg also reports the median of
-calls made after a 1 GiB write has evicted the caches ("flushed"). The
+calls made after a 1 GiB read has evicted the caches ("flushed"). The
 measured ceilings (a pure MFMA loop, a streaming read, a copy) put the rates
 beside what this GPU reaches at all.
 
@@ -128,20 +128,29 @@ def time_steps(fn, steps, warmup):
     return _stats([a.elapsed_time(b) for a, b in ev], start.elapsed_time(end) / steps)
 
 
+def new_flush_buffer(torch):
+    """1 GiB of float32 that time_flushed reads to evict the caches."""
+    return torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+
+
 def time_flushed(fn, steps, flush):
-    """Cold caches: before each timed call, write the whole of `flush` (a
-    1 GiB device buffer), which evicts the L2s and the 256 MB last-level
-    cache; only the call itself sits between its events. None when `flush`
-    is None."""
+    """Cold caches: before each timed call, read the whole of `flush` (1 GiB),
+    which evicts the L2s and the 256 MB last-level cache. A read, not a
+    write: a written buffer would leave up to 256 MB of dirty lines whose
+    write-back then runs during the timed call (that costs a 0.17 ms decode
+    a third of its rate). The read also drains any dirty lines left by
+    earlier calls before the timed one starts. Only the call itself sits
+    between its events. None when `flush` is None."""
     import torch
     if flush is None:
         return None
+    sink = torch.empty(1, dtype=flush.dtype, device=flush.device)
     fn()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
-    for i, (a, b) in enumerate(ev):
-        flush.fill_(i & 0x7F)
+    for a, b in ev:
+        torch.sum(flush, dim=(0,), keepdim=True, out=sink)
         a.record()
         fn()
         b.record()
@@ -399,7 +408,7 @@ def main():
     prefill_src = ("prefill.hip", "pkv_common.h", "launch.h")
     decode_src = ("decode.hip", "pkv_common.h", "launch.h")
     append_src = ("append.hip", "pkv_common.h", "launch.h")
-    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    flush = None if args.no_flush else new_flush_buffer(torch)
     T, G = 1e12, 1e9
 
     print("bench: prefill (bf16, batch 16)", file=sys.stderr, flush=True)
@@ -579,7 +588,7 @@ def only(args, torch, pkv, workloads):
     elif args.only == "ceilings":
         r = measured_ceilings(torch)
     else:  # append_sweep
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+        flush = new_flush_buffer(torch)
         for k in range(12, 21):
             w = workloads.append_sweep("cuda:0", nnz=1 << k)
             nb, step = bench_append(pkv, torch, w)
