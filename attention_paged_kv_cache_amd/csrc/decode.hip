@@ -106,12 +106,18 @@ __device__ __forceinline__ void request_rows(const DecodeArgs &a, int b, int &ql
 // Raw K/V of one 32-key step as loaded (e4m3 bytes or 16-bit values).
 template <bool FP8>
 struct RawKV {
-  using T = typename std::conditional<FP8, u32x2, u32x4>::type;
   // K: 16-byte loads either way: 8 d of one k-step (16-bit) or 16 d of two
   // k-steps (e4m3), [m-block][load]
   u32x4 k[2][FP8 ? 2 : 4];
-  T v[8];     // 8 keys x 8 d
+  // V, 16-byte loads either way: 8 keys x 8 d (16-bit), or 4 keys x 16 d
+  // (e4m3; the two lanes of a pair swap halves to get 8 keys x 8 d each)
+  u32x4 v[FP8 ? 4 : 8];
 };
+
+// The value of the neighbouring lane (lane ^ 1) of a quad.
+__device__ __forceinline__ uint32_t swap_lane1(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+}
 
 // d offset of the 8 query elements lane group g4 feeds to k-step t. For
 // e4m3 K a lane loads 16 consecutive d (one 16-byte load) and feeds its two
@@ -275,11 +281,19 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
       for (int u = 0; u < (FP8 ? 2 : 4); ++u)
         r.k[mb][u] = ld16(kp + kstep_d<FP8>(FP8 ? 2 * u : u, g4) * ES);
     }
-    const char *vp = ((voff >> log2ps) ? vb1 : vb0) + ((kg0 + voff) & ps_mask) * sstr + r16 * 8 * ES;
+    if constexpr (FP8) {
+      // lane pair (2i, 2i+1): d 16i..16i+15, keys 0-3 (even) / 4-7 (odd)
+      // of the pair's 8-key group
+      const int vo = voff + 4 * (r16 & 1);
+      const char *vp =
+          ((vo >> log2ps) ? vb1 : vb0) + ((kg0 + vo) & ps_mask) * sstr + (r16 >> 1) * 16;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      if constexpr (FP8) r.v[jj] = ld8(vp + jj * sstr);
-      else r.v[jj] = ld16(vp + jj * sstr);
+      for (int jj = 0; jj < 4; ++jj) r.v[jj] = ld16(vp + jj * sstr);
+    } else {
+      const char *vp =
+          ((voff >> log2ps) ? vb1 : vb0) + ((kg0 + voff) & ps_mask) * sstr + r16 * 8 * ES;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) r.v[jj] = ld16(vp + jj * sstr);
     }
   };
 
@@ -308,10 +322,22 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
           kop[mb][s] = r.k[mb][s];
         }
       }
+    if constexpr (FP8) {
+      // each lane keeps the 8 d of its own d-run and sends the other 8 to
+      // its partner: even lanes end with keys 0-3 loaded and 4-7 received,
+      // odd lanes the reverse
+      const bool odd = r16 & 1;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      if constexpr (FP8) vrow[jj] = widen8(r.v[jj], QT{});
-      else vrow[jj] = r.v[jj];
+      for (int jj = 0; jj < 4; ++jj) {
+        const u32x4 w = r.v[jj];
+        const u32x2 own = odd ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
+        const u32x2 got = {swap_lane1(odd ? w[0] : w[2]), swap_lane1(odd ? w[1] : w[3])};
+        vrow[jj] = widen8(odd ? got : own, QT{});
+        vrow[4 + jj] = widen8(odd ? own : got, QT{});
+      }
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) vrow[jj] = r.v[jj];
     }
     // keys past the sequence end hold whatever the last page's tail holds:
     // zero them so that p = 0 meets v = 0, never NaN
