@@ -151,12 +151,22 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
   const int g4 = lane >> 4;
   const int r16 = lane & 15;
 
-  // Block -> (unit u = (split, request, kv head), row group). The row groups
-  // of one unit sit 8 blocks apart, so they run on the same XCD, close in
-  // time, and the second streams the unit's K/V from that XCD's L2.
+  // Block -> (unit u = (split, request, kv head), row group). Blocks are
+  // dealt to the 8 XCDs in turn (block i on XCD i % 8).
+  //  * One row group: the kv heads of one (split, request) go to one XCD as
+  //    consecutive blocks, so the pages' K (then V) runs of all heads, which
+  //    are adjacent in an HND page, are read by one XCD close in time.
+  //  * Several row groups: the groups of one unit sit 8 blocks apart, so
+  //    they run on the same XCD, close in time, and the second streams the
+  //    unit's K/V from that XCD's L2.
   const int bh = a.batch * a.num_heads_kv;
-  int u = blockIdx.x, grp = 0;
-  if (n_groups > 1) {
+  int u, grp = 0;
+  if (n_groups == 1) {
+    const int H = a.num_heads_kv;
+    const int slot = blockIdx.x / kXcds;
+    u = ((slot / H) * kXcds + blockIdx.x % kXcds) * H + slot % H;
+    if (u >= bh * max_splits) return;
+  } else {
     const int rest = blockIdx.x / kXcds;
     grp = rest % n_groups;
     u = (rest / n_groups) * kXcds + blockIdx.x % kXcds;
@@ -609,8 +619,10 @@ hipError_t launch_nb(const DecodeArgs &a, const DecodePlan &p, hipStream_t s) {
   if (n_units == 0) return hipSuccess;
   // rows beyond 32 per kv head: groups of 32, each unit's groups on one XCD
   const int n_groups = (p.rows + 31) / 32;
-  const int64_t blocks =
-      n_groups == 1 ? n_units : (n_units + kXcds - 1) / kXcds * kXcds * n_groups;
+  // whole rounds of 8 XCDs x (kv heads or row groups); blocks past the last
+  // unit return at once
+  const int64_t per_round = n_groups == 1 ? (int64_t)kXcds * a.num_heads_kv : kXcds;
+  const int64_t blocks = (n_units + per_round - 1) / per_round * per_round * n_groups;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((decode_kernel<NB, QT, FP8>), dim3((uint32_t)blocks),
                      dim3(kThreads), 0, s, a, p.chunk, p.max_splits, n_groups, ws_o,
@@ -642,12 +654,14 @@ DecodePlan plan_decode(int32_t batch, int32_t q_len, int32_t num_heads_qo,
       window_left >= 0 ? (int64_t)std::min<int64_t>(max_seq_len, (int64_t)window_left + q_len)
                        : (int64_t)max_seq_len;
   const int64_t units = (int64_t)batch * num_heads_kv;
-  // Enough workgroups to fill the chip, but chunks long enough that the
-  // partial (m, l, O) rows, written once and read once by the merge, stay
-  // within 3% of the K/V bytes a chunk streams (at one byte per element;
-  // bf16 caches halve that share). With many query rows per kv head
-  // (drafts x GQA group) this leaves one chunk per request: no merge.
-  int64_t c_bal = units > 0 ? (max_keys * units + 16383) / 16384 : max_keys;
+  // About 8192 workgroups at the longest request (32 per CU: enough to
+  // balance ragged lengths; more, shorter chunks measured slower), but
+  // chunks long enough that the partial (m, l, O) rows, written once and
+  // read once by the merge, stay within 3% of the K/V bytes a chunk streams
+  // (at one byte per element; bf16 caches halve that share). With many
+  // query rows per kv head (drafts x GQA group) this leaves one chunk per
+  // request: no merge.
+  int64_t c_bal = units > 0 ? (max_keys * units + 8191) / 8192 : max_keys;
   const int64_t kv_bytes_per_key = 2 * (int64_t)head_dim;
   int64_t c_min = 2 * (int64_t)p.rows * (head_dim + 2) * 4 * 100 / (3 * kv_bytes_per_key);
   int64_t chunk = std::max<int64_t>(c_bal, c_min);
