@@ -47,8 +47,18 @@ def _layout(name):
         raise ValueError(f"kv_layout must be 'NHD' or 'HND', got {name!r}") from None
 
 
-def _stream():
-    return torch.cuda.current_stream().cuda_stream
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _on_gpu(device, **tensors):
+    """Raise unless ``device`` is a GPU and every given tensor lives on it:
+    the library reads its pointer arguments as device memory."""
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {device}")
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
 def _ptr(t):
@@ -91,38 +101,47 @@ def _cache_dims(k, layout):
 
 def get_seq_lens(kv_indptr, kv_last_page_len, page_size):
     """Tokens of each request: (pages - 1) * page_size + last_page_len."""
-    indptr = _i32_on(kv_indptr, kv_last_page_len.device)
-    last = _i32_on(kv_last_page_len, kv_last_page_len.device)
-    out = torch.empty(last.shape[0], dtype=torch.int32, device=last.device)
-    _lib.check(_lib.load().pkv_get_seq_lens(_ptr(indptr), _ptr(last), last.shape[0],
-                                            int(page_size), _ptr(out), _stream()),
-               "get_seq_lens")
+    dev = kv_last_page_len.device
+    _on_gpu(dev)
+    indptr = _i32_on(kv_indptr, dev)
+    last = _i32_on(kv_last_page_len, dev)
+    out = torch.empty(last.shape[0], dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.load().pkv_get_seq_lens(_ptr(indptr), _ptr(last), last.shape[0],
+                                                int(page_size), _ptr(out), _stream(dev)),
+                   "get_seq_lens")
     return out
 
 
 def get_batch_indices_positions(append_indptr, seq_lens, nnz):
     """(batch_indices, positions) of the appended rows; positions are the
     last append-length positions of each request."""
-    ai = _i32_on(append_indptr, seq_lens.device)
-    seq = _i32_on(seq_lens, seq_lens.device)
-    bi = torch.empty(int(nnz), dtype=torch.int32, device=seq.device)
-    pos = torch.empty(int(nnz), dtype=torch.int32, device=seq.device)
-    _lib.check(_lib.load().pkv_get_batch_indices_positions(
-        _ptr(ai), _ptr(seq), seq.shape[0], int(nnz), _ptr(bi), _ptr(pos), _stream()),
-        "get_batch_indices_positions")
+    dev = seq_lens.device
+    _on_gpu(dev)
+    ai = _i32_on(append_indptr, dev)
+    seq = _i32_on(seq_lens, dev)
+    bi = torch.empty(int(nnz), dtype=torch.int32, device=dev)
+    pos = torch.empty(int(nnz), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.load().pkv_get_batch_indices_positions(
+            _ptr(ai), _ptr(seq), seq.shape[0], int(nnz), _ptr(bi), _ptr(pos), _stream(dev)),
+            "get_batch_indices_positions")
     return bi, pos
 
 
 def csr_to_block_tables(kv_indptr, kv_indices, max_pages_per_seq):
     """Dense block_tables [batch, max_pages_per_seq] from kv_indptr/kv_indices
     (entries past a request's pages are -1)."""
-    indptr = _i32_on(kv_indptr, kv_indices.device)
-    idx = _i32_on(kv_indices, kv_indices.device)
+    dev = kv_indices.device
+    _on_gpu(dev)
+    indptr = _i32_on(kv_indptr, dev)
+    idx = _i32_on(kv_indices, dev)
     batch = indptr.shape[0] - 1
-    bt = torch.empty(batch, int(max_pages_per_seq), dtype=torch.int32, device=idx.device)
-    _lib.check(_lib.load().pkv_csr_to_block_tables(
-        _ptr(indptr), _ptr(idx), batch, int(max_pages_per_seq), _ptr(bt), _stream()),
-        "csr_to_block_tables")
+    bt = torch.empty(batch, int(max_pages_per_seq), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.load().pkv_csr_to_block_tables(
+            _ptr(indptr), _ptr(idx), batch, int(max_pages_per_seq), _ptr(bt), _stream(dev)),
+            "csr_to_block_tables")
     return bt
 
 
@@ -137,14 +156,16 @@ def append_paged_kv_cache(append_key, append_value, batch_indices, positions,
         raise ValueError("append rows and cache must share one dtype")
     if tuple(append_key.shape[1:]) != (hkv, d) or append_value.shape != append_key.shape:
         raise ValueError("append_key/append_value must be [nnz, num_kv_heads, head_dim]")
-    ak, av = append_key.contiguous(), append_value.contiguous()
     dev = k.device
+    _on_gpu(dev, v_cache=v, append_key=append_key, append_value=append_value)
+    ak, av = append_key.contiguous(), append_value.contiguous()
     bi, pos = _i32_on(batch_indices, dev), _i32_on(positions, dev)
     idx, indptr = _i32_on(kv_indices, dev), _i32_on(kv_indptr, dev)
-    _lib.check(_lib.load().pkv_append_paged_kv_cache(
-        _ptr(ak), _ptr(av), _ptr(bi), _ptr(pos), ak.shape[0], _ptr(k), _ptr(v), psk, psv,
-        _ptr(idx), _ptr(indptr), None, indptr.shape[0] - 1, hkv, d, ps, layout, _dt(k),
-        _stream()), "append_paged_kv_cache")
+    with torch.cuda.device(dev):
+        _lib.check(_lib.load().pkv_append_paged_kv_cache(
+            _ptr(ak), _ptr(av), _ptr(bi), _ptr(pos), ak.shape[0], _ptr(k), _ptr(v), psk, psv,
+            _ptr(idx), _ptr(indptr), None, indptr.shape[0] - 1, hkv, d, ps, layout, _dt(k),
+            _stream(dev)), "append_paged_kv_cache")
 
 
 def prefill_workspace_size(batch_size):
@@ -220,6 +241,8 @@ def batch_prefill_with_kv_cache(q, k_cache, v_cache, scale, workspace_buffer, *,
     if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.dim() != 2 or \
             lse.shape[1] != h_qo:
         raise ValueError("lse must be a contiguous float32 [rows, num_heads_qo] tensor")
+    _on_gpu(dev, k_cache=k_cache, v_cache=v_cache, workspace_buffer=workspace_buffer,
+            out=out, lse=lse)
     lq = _i32_on(actual_seq_lens_q, dev)
     lkv = _i32_on(actual_seq_lens_kv, dev)
     bt = _i32_on(block_tables, dev) if paged else None
@@ -230,17 +253,17 @@ def batch_prefill_with_kv_cache(q, k_cache, v_cache, scale, workspace_buffer, *,
         if o is not None and o.shape[0] != lq.shape[0]:
             raise ValueError("batch offsets must have batch_size entries")
     keep = []
-    _lib.check(_lib.load().pkv_batch_prefill_with_kv_cache(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), k_cache.stride(0) if paged else 0,
-        v_cache.stride(0) if paged else 0, float(scale), _ptr(workspace_buffer),
-        workspace_buffer.numel() * workspace_buffer.element_size(),
-        int(max_token_per_sequence), int(max_sequence_kv), _ptr(lq), _ptr(lkv),
-        _ptr(bt) if paged else None, bt.shape[1] if paged else 0, lq.shape[0], h_qo, hkv,
-        d_qk, d_vo, ps, layout, 1 if causal else 0,
-        _scale_ptr(q_scale, dev, keep), _scale_ptr(k_scale, dev, keep),
-        _scale_ptr(v_scale, dev, keep), _ptr(out), _ptr(lse), _dt(q), _dt(out),
-        *[None if o is None else _ptr(o) for o in offs], _stream()),
-        "batch_prefill_with_kv_cache")
+    scales = [_scale_ptr(x, dev, keep) for x in (q_scale, k_scale, v_scale)]
+    with torch.cuda.device(dev):
+        _lib.check(_lib.load().pkv_batch_prefill_with_kv_cache(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), k_cache.stride(0) if paged else 0,
+            v_cache.stride(0) if paged else 0, float(scale), _ptr(workspace_buffer),
+            workspace_buffer.numel() * workspace_buffer.element_size(),
+            int(max_token_per_sequence), int(max_sequence_kv), _ptr(lq), _ptr(lkv),
+            _ptr(bt) if paged else None, bt.shape[1] if paged else 0, lq.shape[0], h_qo, hkv,
+            d_qk, d_vo, ps, layout, 1 if causal else 0, *scales, _ptr(out), _ptr(lse),
+            _dt(q), _dt(out), *[None if o is None else _ptr(o) for o in offs], _stream(dev)),
+            "batch_prefill_with_kv_cache")
     return out, lse
 
 
@@ -300,6 +323,7 @@ def batch_decode_with_kv_cache(query, kv_cache, workspace_buffer, block_tables, 
         out = torch.empty(query.shape[0], h_qo, d, dtype=out_dtype, device=dev)
     if out.dtype != out_dtype or not out.is_contiguous() or tuple(out.shape) != tuple(query.shape):
         raise ValueError("out must be a contiguous tensor shaped like query")
+    _on_gpu(dev, k_cache=k, v_cache=v, workspace_buffer=workspace_buffer, out=out)
     bt = _i32_on(block_tables, dev)
     seq = seq_lens.to(dev)
     if seq.dtype not in (torch.int32, torch.uint32):
@@ -317,13 +341,14 @@ def batch_decode_with_kv_cache(query, kv_cache, workspace_buffer, block_tables, 
         sink_ptr = sinks.data_ptr()
     b1, b1_ptr = _scale_arg(bmm1_scale, dev, "bmm1_scale")
     b2, b2_ptr = _scale_arg(bmm2_scale, dev, "bmm2_scale")
-    _lib.check(_lib.load().pkv_batch_decode_with_kv_cache(
-        _ptr(query), _ptr(k), _ptr(v), psk, psv, _ptr(workspace_buffer),
-        workspace_buffer.numel() * workspace_buffer.element_size(), _ptr(bt), bt.shape[1],
-        _ptr(seq), batch, int(max_seq_len), b1, b2, int(window_left), _ptr(out), _dt(out),
-        sink_ptr, layout, int(q_len_per_req), h_qo, hkv, d, ps, _dt(query), _dt(k), b1_ptr,
-        b2_ptr, float(o_scale), None if cum is None else cum.data_ptr(),
-        0 if cum is None else q_max, mask_ptr, _stream()), "batch_decode_with_kv_cache")
+    with torch.cuda.device(dev):
+        _lib.check(_lib.load().pkv_batch_decode_with_kv_cache(
+            _ptr(query), _ptr(k), _ptr(v), psk, psv, _ptr(workspace_buffer),
+            workspace_buffer.numel() * workspace_buffer.element_size(), _ptr(bt), bt.shape[1],
+            _ptr(seq), batch, int(max_seq_len), b1, b2, int(window_left), _ptr(out), _dt(out),
+            sink_ptr, layout, int(q_len_per_req), h_qo, hkv, d, ps, _dt(query), _dt(k), b1_ptr,
+            b2_ptr, float(o_scale), None if cum is None else cum.data_ptr(),
+            0 if cum is None else q_max, mask_ptr, _stream(dev)), "batch_decode_with_kv_cache")
     return out
 
 
