@@ -581,20 +581,48 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a,
   const int64_t orow = (int64_t)(qrow0 + qi) * a.num_heads_qo + head;
   if (n_splits == 1) return;  // written by the split kernel
   const int64_t unit0 = ((int64_t)b * a.num_heads_kv + kvh) * max_splits;
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, ws_ml[((unit0 + s) * rows + n) * 2]);
+  // One pass over the splits with a running maximum M (starting at the
+  // sink logit), four splits' loads in flight at a time: L and O are
+  // rescaled by 2^(M_old - M_new) whenever M rises.
   const float sink = a.sinks ? a.sinks[head] * kLog2e : -INFINITY;
-  const float M_all = fmaxf(M, sink);
-  const float M_use = (M_all == -INFINITY) ? 0.0f : M_all;
-  float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int s = 0; s < n_splits; ++s) {
-    const int64_t u = (unit0 + s) * rows + n;
-    const float f = fast_exp2(ws_ml[u * 2] - M_use);
-    L += f * ws_ml[u * 2 + 1];
-    const f32x2 v = *reinterpret_cast<const f32x2 *>(ws_o + u * kD + lane * 2);
-    o0 += f * v[0];
-    o1 += f * v[1];
+  float M = sink, L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  int s = 0;
+  for (; s + 4 <= n_splits; s += 4) {
+    f32x2 ml[4], v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t u = (unit0 + s + i) * rows + n;
+      ml[i] = *reinterpret_cast<const f32x2 *>(ws_ml + u * 2);
+      v[i] = *reinterpret_cast<const f32x2 *>(ws_o + u * kD + lane * 2);
+    }
+    const float Mn = fmaxf(fmaxf(M, fmaxf(ml[0][0], ml[1][0])), fmaxf(ml[2][0], ml[3][0]));
+    const float Mu = Mn == -INFINITY ? 0.0f : Mn;
+    const float r = fast_exp2(M - Mu);
+    L *= r;
+    o0 *= r;
+    o1 *= r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float f = fast_exp2(ml[i][0] - Mu);
+      L += f * ml[i][1];
+      o0 += f * v[i][0];
+      o1 += f * v[i][1];
+    }
+    M = Mn;
   }
+  for (; s < n_splits; ++s) {
+    const int64_t u = (unit0 + s) * rows + n;
+    const f32x2 ml = *reinterpret_cast<const f32x2 *>(ws_ml + u * 2);
+    const f32x2 v = *reinterpret_cast<const f32x2 *>(ws_o + u * kD + lane * 2);
+    const float Mn = fmaxf(M, ml[0]);
+    const float Mu = Mn == -INFINITY ? 0.0f : Mn;
+    const float r = fast_exp2(M - Mu), f = fast_exp2(ml[0] - Mu);
+    L = L * r + f * ml[1];
+    o0 = o0 * r + f * v[0];
+    o1 = o1 * r + f * v[1];
+    M = Mn;
+  }
+  const float M_use = (M == -INFINITY) ? 0.0f : M;
   if (a.sinks) L += fast_exp2(sink - M_use);
   const float bmm2 = a.bmm2_ptr ? a.bmm2_ptr[0] : a.bmm2_scale;
   if (a.out_dtype == 2) {
