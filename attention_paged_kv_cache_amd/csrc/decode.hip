@@ -336,53 +336,27 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
   }
 
   auto compute = [&](const RawKV<FP8> &r, int kg0) {
-    u32x4 kop[2][4], vrow[8];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if constexpr (FP8) {
-          const u32x4 w = r.k[mb][s >> 1];
-          kop[mb][s] = widen8((s & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]}, QT{});
-        } else {
-          kop[mb][s] = r.k[mb][s];
-        }
-      }
-    if constexpr (FP8) {
-      // each lane keeps the 8 d of its own d-run and sends the other 8 to
-      // its partner: even lanes end with keys 0-3 loaded and 4-7 received,
-      // odd lanes the reverse
-      const bool odd = r16 & 1;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const u32x4 w = r.v[jj];
-        const u32x2 own = odd ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
-        const u32x2 got = {swap_lane1(odd ? w[0] : w[2]), swap_lane1(odd ? w[1] : w[3])};
-        vrow[jj] = widen8(odd ? got : own, QT{});
-        vrow[4 + jj] = widen8(odd ? own : got, QT{});
-      }
-    } else {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) vrow[jj] = r.v[jj];
-    }
-    // keys past the sequence end hold whatever the last page's tail holds:
-    // zero them so that p = 0 meets v = 0, never NaN
-    if (kg0 + 32 > seq) {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        if (kg0 + voff + jj >= seq) vrow[jj] = u32x4{0u, 0u, 0u, 0u};
-    }
-
-    // ---- S^T = K Q^T -------------------------------------------------------
+    // ---- S^T = K Q^T (e4m3 K widened one k-step at a time, right before
+    // its MFMAs; V is widened and transposed after the softmax, so neither
+    // holds registers across the other's work) --------------------------------
     f32x4 sacc[2][NB];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < NB; ++nb) sacc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma16(kop[mb][s], qop[nb][s], acc, QT{});
-        sacc[mb][nb] = acc;
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 kop;
+        if constexpr (FP8) {
+          const u32x4 w = r.k[mb][s >> 1];
+          kop = widen8((s & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]}, QT{});
+        } else {
+          kop = r.k[mb][s];
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) sacc[mb][nb] = mfma16(kop, qop[nb][s], sacc[mb][nb], QT{});
       }
 
     // ---- mask where the step crosses a boundary ----------------------------
@@ -439,6 +413,32 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
     }
 
     // ---- O^T += V^T P^T --------------------------------------------------------
+    u32x4 vrow[8];
+    if constexpr (FP8) {
+      // each lane keeps the 8 d of its own d-run and sends the other 8 to
+      // its partner: even lanes end with keys 0-3 loaded and 4-7 received,
+      // odd lanes the reverse
+      const bool odd = r16 & 1;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const u32x4 w = r.v[jj];
+        const u32x2 own = odd ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
+        const u32x2 got = {swap_lane1(odd ? w[0] : w[2]), swap_lane1(odd ? w[1] : w[3])};
+        vrow[jj] = widen8(odd ? got : own, QT{});
+        vrow[4 + jj] = widen8(odd ? own : got, QT{});
+      }
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) vrow[jj] = r.v[jj];
+    }
+    // keys past the sequence end hold whatever the last page's tail holds:
+    // zero them so that p = 0 meets v = 0, never NaN
+    if (kg0 + 32 > seq) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        if (kg0 + voff + jj >= seq) vrow[jj] = u32x4{0u, 0u, 0u, 0u};
+    }
+
     u32x4 vt[8];
     transpose8x8_b16(vrow, vt);
 #pragma unroll

@@ -328,8 +328,8 @@ def measured_ceilings(torch, steps=10):
     return {"mfma_bf16_loop_TFLOPs": round(mfma, 1), "hbm_read_4GiB_GBs": round(read, 1),
             "hbm_copy_1GiB_GBs": round(copy, 1),
             "what": "pure v_mfma_f32_32x32x16_bf16 loop (8 chains per wave, 8192 waves); "
-                    "streaming 16-byte loads over 4 GiB (2048 workgroups, one contiguous span "
-                    "each); torch copy_ of 1 GiB (read + write counted); medians of 10 calls"}
+                    "non-temporal 16-byte loads over 4 GiB (2048 workgroups, one contiguous "
+                    "span each); torch copy_ of 1 GiB (read + write counted); medians of 10 calls"}
 
 
 def cpu_baseline(w, budget_s=12.0):
