@@ -19,11 +19,15 @@
 //   range starts at seq - q_len - window_left). A workgroup of 4 waves owns
 //   one unit; each wave streams chunk/4 keys, 32 at a time, straight from
 //   global memory into MFMA operands (no LDS on the streaming path):
-//     K: lane = (key, 8-element d run): 16-byte loads (8 bytes for e4m3,
-//        widened exactly to bf16 in registers).
-//     V: lane = (8 keys, 8-element d run): 8 loads, then an 8x8 transpose
-//        in registers gives V^T operands whose k-run is 8 consecutive keys.
+//     K: lane = (key, d run): 16-byte loads (8 d of one MFMA k-step, or
+//        16 e4m3 d feeding two k-steps, widened exactly to the query's
+//        16-bit type in registers).
+//     V: lane = (8 keys, 8-element d run): 16-byte loads (e4m3: a lane
+//        pair swaps halves to get there), then an 8x8 transpose in
+//        registers gives V^T operands whose k-run is 8 consecutive keys.
 //     S^T = K Q^T, online softmax in fp32 (base 2), O^T += V^T P^T.
+//   With one row group per unit the K/V loads are non-temporal (streaming):
+//   each byte is read once per call.
 //   The four waves' (m, l, O) are merged in LDS. A request that fits one
 //   unit writes its output directly; otherwise the unit writes its partial
 //   (m, l, O) to the workspace and a merge kernel combines the splits and
