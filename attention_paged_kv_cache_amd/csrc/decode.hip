@@ -49,6 +49,7 @@ constexpr int kThreads = 256;
 constexpr int kXcds = 8;  // workgroups are dispatched round-robin over 8 XCDs
 constexpr int kWaves = 4;
 constexpr int kD = 128;
+constexpr float kLazy = 8.0f;  // see the online softmax in decode_kernel
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c, BF16Tag) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -396,10 +397,20 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
         for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sacc[mb][nb][i]);
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_run[nb], mloc * c);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = fast_exp2(m_run[nb] - m_use);
-      m_run[nb] = m_new;
+      // The reference maximum m_run is raised lazily: only when this step's
+      // maximum exceeds it by more than kLazy (log2 units), so most steps
+      // skip rescaling O and exponentials stay <= 2^kLazy.
+      const float m_tile = mloc * c;  // -inf when every key of the row is masked
+      const bool need = m_tile > m_run[nb] + kLazy;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? m_tile : m_run[nb];
+        const float alpha = need ? fast_exp2(m_run[nb] - m_new) : 1.0f;
+        m_run[nb] = m_new;
+        l_run[nb] *= alpha;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) o[cc][nb] *= alpha;
+      }
+      const float m_use = (m_run[nb] == -INFINITY) ? 0.0f : m_run[nb];
       float ps = 0.0f;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
@@ -411,9 +422,7 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
         pop[nb][2 * mb] = pack2(p0, p1, QT{});
         pop[nb][2 * mb + 1] = pack2(p2, p3, QT{});
       }
-      l_run[nb] = l_run[nb] * alpha + ps;
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc) o[cc][nb] *= alpha;
+      l_run[nb] += ps;
     }
 
     // ---- O^T += V^T P^T --------------------------------------------------------

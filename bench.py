@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--settle-ms", type=float, default=250.0,
+                   help="untimed back-to-back calls of each workload for at least this long "
+                        "before its warm-up steps (0: none; profiling runs pass 0)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-flush", action="store_true",
                    help="skip the cold-cache timings and the measured ceilings (kernel traces)")
@@ -105,12 +108,37 @@ def _stats(per, region_ms):
     return Timing(region_ms, sum(per) / len(per), per[0], statistics.median(per))
 
 
+# Untimed back-to-back calls before each workload's warm-up steps, in ms (set
+# from --settle-ms). The host builds each workload for seconds while the GPU
+# idles; after such a gap the GPU's clocks go through a transient of 20 to
+# 40 ms (measured: speculative decode ran one fast 20-call window, then
+# 5.0 TB/s, recovering to its steady 5.8 over about 160 calls; the first
+# prefill round read 851 to 857 TFLOP/s against about 935 after), longer
+# than 10 warm-up calls of the short workloads. Settling first makes every
+# leg a steady-state measurement.
+SETTLE_MS = 250.0
+
+
+def settle(fn):
+    """Call `fn` back to back, untimed, for at least SETTLE_MS of wall time."""
+    import torch
+    if SETTLE_MS <= 0:
+        return
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < SETTLE_MS:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_steps(fn, steps, warmup):
-    """Warm caches: `warmup` untimed calls, then `steps` calls back to back.
+    """Warm caches: settle (see SETTLE_MS), `warmup` untimed calls, then `steps`
+    calls back to back.
     region_ms is the whole region per step; launch/min/median_ms come from
     events around each call. Events sit on the current stream, which is the
     stream the library enqueues on."""
     import torch
+    settle(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -392,7 +420,9 @@ def rate(work, ms, scale):
 
 
 def main():
+    global SETTLE_MS
     args = parse()
+    SETTLE_MS = args.settle_ms
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -481,6 +511,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(t1.region_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
