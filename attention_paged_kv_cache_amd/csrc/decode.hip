@@ -25,7 +25,8 @@
 //     V: lane = (8 keys, 8-element d run): 16-byte loads (e4m3: a lane
 //        pair swaps halves to get there), then an 8x8 transpose in
 //        registers gives V^T operands whose k-run is 8 consecutive keys.
-//     S^T = K Q^T, online softmax in fp32 (base 2), O^T += V^T P^T.
+//     S^T = K Q^T, online softmax in fp32 (base 2; the reference maximum
+//     is raised lazily, so most steps skip rescaling O), O^T += V^T P^T.
 //   With one row group per unit the K/V loads are non-temporal (streaming):
 //   each byte is read once per call.
 //   The four waves' (m, l, O) are merged in LDS. A request that fits one
