@@ -251,12 +251,17 @@ PKV_API pkv_status pkv_batch_prefill_with_kv_cache(
   int32_t *cum_q = reinterpret_cast<int32_t *>(workspace);
   int32_t *cum_kv = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(workspace) +
                                                 prefill_region_bytes(batch_size));
-  a.off_q = batch_offsets_q ? batch_offsets_q : cum_q;
-  a.off_o = batch_offsets_o ? batch_offsets_o : cum_q;
-  a.off_lse = batch_offsets_stats ? batch_offsets_stats : cum_q;
+  // Absent offsets mean packed rows: small batches leave them null and the
+  // kernel sums the lengths itself; larger ones get a prefix-sum launch.
+  const bool inline_offsets = batch_size <= pkv::kInlineOffsetBatch;
+  int32_t *packed_q = inline_offsets ? nullptr : cum_q;
+  int32_t *packed_kv = inline_offsets ? nullptr : cum_kv;
+  a.off_q = batch_offsets_q ? batch_offsets_q : packed_q;
+  a.off_o = batch_offsets_o ? batch_offsets_o : packed_q;
+  a.off_lse = batch_offsets_stats ? batch_offsets_stats : packed_q;
   a.block_tables = block_tables;
-  a.off_k = batch_offsets_k ? batch_offsets_k : cum_kv;
-  a.off_v = batch_offsets_v ? batch_offsets_v : cum_kv;
+  a.off_k = batch_offsets_k ? batch_offsets_k : packed_kv;
+  a.off_v = batch_offsets_v ? batch_offsets_v : packed_kv;
   a.max_pages = max_pages_per_seq;
   a.batch = batch_size;
   a.num_heads_qo = num_heads_qo;
@@ -275,11 +280,11 @@ PKV_API pkv_status pkv_batch_prefill_with_kv_cache(
   a.qkv_dtype = qkv_dtype;
   a.o_dtype = o_dtype;
   hipStream_t s = as_stream(stream);
-  if (!batch_offsets_q || !batch_offsets_o || !batch_offsets_stats) {
+  if (!inline_offsets && (!batch_offsets_q || !batch_offsets_o || !batch_offsets_stats)) {
     const hipError_t e = pkv::launch_exclusive_cumsum(actual_seq_lens_q, batch_size, cum_q, s);
     if (e != hipSuccess) return from_hip(e, __func__);
   }
-  if (!paged && (!batch_offsets_k || !batch_offsets_v)) {
+  if (!inline_offsets && !paged && (!batch_offsets_k || !batch_offsets_v)) {
     const hipError_t e =
         pkv::launch_exclusive_cumsum(actual_seq_lens_kv, batch_size, cum_kv, s);
     if (e != hipSuccess) return from_hip(e, __func__);

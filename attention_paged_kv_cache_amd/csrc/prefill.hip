@@ -202,6 +202,18 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   if (tok0 >= L_q) return;
   const int G = a.num_heads_qo / a.num_heads_kv;
   const int tok_last = min(L_q, tok0 + T) - 1;
+  // First rows of request b: given offsets, or packed rows (null offsets,
+  // small batches): the sum of the lengths of the requests before b.
+  auto packed_row = [&](const int32_t *lens) {
+    int r0 = 0;
+    for (int i = 0; i < b; ++i) r0 += lens[i];
+    return r0;
+  };
+  const bool any_packed_q = !a.off_q || !a.off_o || !a.off_lse;
+  const int packed_q = any_packed_q ? packed_row(a.lens_q) : 0;
+  const int row_q = a.off_q ? a.off_q[b] : packed_q;
+  const int row_o = a.off_o ? a.off_o[b] : packed_q;
+  const int row_lse = a.off_lse ? a.off_lse[b] : packed_q;
   const int shift = L_kv - L_q;  // bottom-right alignment
 
   // ---- this lane's query row ---------------------------------------------
@@ -227,7 +239,7 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   // ---- Q^T operand in registers -------------------------------------------
   u32x4 qreg[G_::NQ];
   {
-    const int64_t qrow = (int64_t)(a.off_q[b] + tok) * a.num_heads_qo + head;
+    const int64_t qrow = (int64_t)(row_q + tok) * a.num_heads_qo + head;
     const char *qp = (const char *)a.q + qrow * G_::ROWB;
     const uint32_t flip = negate ? (ES == 1 ? 0x80808080u : 0x80008000u) : 0u;
 #pragma unroll
@@ -272,8 +284,12 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   };
   // Without paging each wave's 16 keys are 16 consecutive rows from
   // off_k[b] + key (off_v[b] + key for values).
-  const int row_k = PAGED ? 0 : a.off_k[b];
-  const int row_v = PAGED ? 0 : a.off_v[b];
+  int row_k = 0, row_v = 0;
+  if constexpr (!PAGED) {
+    const int packed_kv = (!a.off_k || !a.off_v) ? packed_row(a.lens_kv) : 0;
+    row_k = a.off_k ? a.off_k[b] : packed_kv;
+    row_v = a.off_v ? a.off_v[b] : packed_kv;
+  }
 
   // Per-lane source rows / columns of each 1 KB LDS DMA of this wave's 16 K
   // rows (a whole number of KB per wave: lanes that fall in the row padding
@@ -509,7 +525,7 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   const float l_tot = wave_sum_xor32(l_run);
   if (!row_ok) return;
   const float inv = l_tot > 0.0f ? vs / l_tot : 0.0f;
-  const int64_t orow = (int64_t)(a.off_o[b] + tok) * a.num_heads_qo + head;
+  const int64_t orow = (int64_t)(row_o + tok) * a.num_heads_qo + head;
   char *op = (char *)a.out + orow * kDvo * 2;
 #pragma unroll
   for (int md = 0; md < 4; ++md)
@@ -522,7 +538,7 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
       st8(op + d * 2, w);
     }
   if (half == 0)
-    a.lse[(int64_t)(a.off_lse[b] + tok) * a.num_heads_qo + head] =
+    a.lse[(int64_t)(row_lse + tok) * a.num_heads_qo + head] =
         l_tot > 0.0f ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
 }
 

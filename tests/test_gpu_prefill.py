@@ -57,6 +57,18 @@ def check(pkv, w, o_dtype=None):
     return out, lse
 
 
+@pytest.mark.parametrize("batch", [64, 65, 80])
+def test_packed_offsets_on_both_sides_of_the_inline_limit(pkv, batch):
+    """Without batch offsets the requests' rows are packed. Up to 64
+    requests the kernel sums the lengths before its request itself; beyond
+    that a prefix-sum launch writes the offsets to the workspace. Both match
+    the oracle, zero-length requests included."""
+    w = small_prefill(seed=40 + batch, batch=batch, q_len=(0, 40), prefix=(0, 60),
+                      pool_pages=batch * 8 + 8)
+    assert int((w["seq_lens_q"] == 0).sum()) > 0
+    check(pkv, w)
+
+
 def test_append_example_then_prefill_fp16_nhd(pkv):
     w = workloads.append_example(DEV)
     cache = w["paged_kv_cache"]

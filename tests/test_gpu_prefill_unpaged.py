@@ -75,6 +75,21 @@ def test_unpaged_equals_paged_bitwise(pkv, seed, kw):
     assert torch.equal(lse_p.view(torch.int32), lse_u.view(torch.int32))
 
 
+def test_unpaged_packed_offsets_past_the_inline_limit(pkv):
+    """80 requests: the packed q and key/value row offsets come from the
+    prefix-sum launches, not from the in-kernel sum; the unpaged run still
+    equals the paged one bitwise."""
+    w = workloads.batch_prefill(DEV, seed=116, batch=80, q_len=(0, 40), prefix=(0, 60),
+                                pool_pages=720)
+    out_p, lse_p = run_prefill(pkv, w)
+    bt = w["block_tables"]
+    k = contiguous_rows(w["k_cache"], bt, w["seq_lens_kv"], w["layout"])
+    v = contiguous_rows(w["v_cache"], bt, w["seq_lens_kv"], w["layout"])
+    out_u, lse_u = unpaged_call(pkv, w, k, v)
+    assert torch.equal(out_p.view(torch.int16), out_u.view(torch.int16))
+    assert torch.equal(lse_p.view(torch.int32), lse_u.view(torch.int32))
+
+
 def _place(lens, order, gap):
     offs = np.zeros(len(lens), dtype=np.int64)
     cur = 0
