@@ -21,9 +21,11 @@
 //   that page. Every DMA instruction is a full one (keys past the sequence
 //   end reload the last key; their scores are masked), so the loads carry
 //   no branches and are spread between the MFMAs of the previous tile
-//   instead of arriving as one burst. K rows are padded by 16 bytes so that
-//   the 16 rows one read touches fall in distinct banks; each wave's 16 K
-//   rows occupy a whole number of KB. V rows stay in the
+//   instead of arriving as one burst. So that the 16 K rows one read
+//   touches fall in distinct banks, 256-byte K rows (16-bit d 128) keep
+//   their 16-byte chunks XOR-swizzled by row (16 rows fill exactly 4 KB);
+//   other K rows are padded by 16 bytes, and each wave's 16 K rows occupy a
+//   whole number of KB. V rows stay in the
 //   cache's [key][d] order with a 16-byte-chunk XOR swizzle, and the PV
 //   operand (V^T, keys along k) is read with the LDS transpose reads
 //   ds_read_b64_tr_b16 (ds_read_b64_tr_b8 for e4m3, widened after the read).
@@ -81,7 +83,10 @@ template <class ET, int DQK>
 struct Geo {
   static constexpr int ES = ET::bytes;
   static constexpr int ROWB = DQK * ES;                 // bytes of one K row
-  static constexpr int KRB = ROWB + 16;                 // padded K row in LDS
+  // 256-byte K rows: unpadded, 16-byte chunks XOR-swizzled by row (16 rows
+  // fill exactly 4 KB: four DMAs per wave); other widths: padded by 16 B
+  static constexpr bool KSWZ = ROWB == 256;
+  static constexpr int KRB = KSWZ ? ROWB : ROWB + 16;   // K row in LDS
   static constexpr int VRB = kDvo * ES;                 // V row (unpadded, swizzled)
   static constexpr int KB = (ES == 1) ? 32 : 16;        // k bytes per lane per MFMA
   static constexpr int KSTEPS = ROWB / (2 * KB);        // MFMA k-steps for QK^T
@@ -300,8 +305,12 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   for (int q = 0; q < G_::K_INSTR; ++q) {
     const int byte = q * 1024 + lane * 16;
     int row = byte / G_::KRB, col = byte - row * G_::KRB;
-    if (row > 15) { row = 15; col = 0; }
-    if (col >= G_::ROWB) col = G_::ROWB - 16;
+    if constexpr (G_::KSWZ) {
+      col = (((col >> 4) ^ row) & 15) * 16;  // LDS chunk c of row r holds chunk c ^ r
+    } else {
+      if (row > 15) { row = 15; col = 0; }
+      if (col >= G_::ROWB) col = G_::ROWB - 16;
+    }
     k_row[q] = row;
     k_col[q] = col;
   }
@@ -408,14 +417,20 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
     {
       const int kr = key_perm(l32);
       const char *krow0 = lds_k + (kr >> 4) * G_::WKB + (kr & 15) * G_::KRB;
+      // swizzled rows: logical chunk 2s + half sits at chunk (2s) ^ kx
+      const int kx = half ^ (kr & 15);
 #pragma unroll
       for (int s = 0; s < G_::KSTEPS; ++s) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
           u32x4 av[2];
+          if constexpr (G_::KSWZ) {
+            av[0] = ld16(krow0 + mb * 2 * G_::WKB + 16 * ((2 * s) ^ kx));
+          } else {
 #pragma unroll
-          for (int u = 0; u < G_::KB / 16; ++u)
-            av[u] = ld16(krow0 + mb * 2 * G_::WKB + s * 2 * G_::KB + half * G_::KB + 16 * u);
+            for (int u = 0; u < G_::KB / 16; ++u)
+              av[u] = ld16(krow0 + mb * 2 * G_::WKB + s * 2 * G_::KB + half * G_::KB + 16 * u);
+          }
           sacc[mb] = mfma_qk(av, &qreg[s * (G_::KB / 16)], sacc[mb], ET{});
         }
       }
