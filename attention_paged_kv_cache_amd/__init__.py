@@ -34,10 +34,14 @@ _LAYOUTS = {"NHD": NHD, "HND": HND}
 
 
 def _dt(t):
+    return _dtc(t.dtype)
+
+
+def _dtc(dtype):
     try:
-        return _DTYPES[t.dtype]
+        return _DTYPES[dtype]
     except KeyError:
-        raise ValueError(f"unsupported dtype {t.dtype}") from None
+        raise ValueError(f"unsupported dtype {dtype}") from None
 
 
 def _layout(name):
@@ -48,7 +52,18 @@ def _layout(name):
 
 
 def _stream(device):
-    return torch.cuda.current_stream(device).cuda_stream
+    """Raw handle of the current HIP stream of ``device`` (what the library
+    enqueues on)."""
+    return torch._C._cuda_getCurrentRawStream(device.index)
+
+
+def _call(device, fn, *args):
+    """Call ``fn(*args)`` with ``device`` current (a launch on the null stream
+    goes to the current device); skips the device switch when it already is."""
+    if torch._C._cuda_getDevice() == device.index:
+        return fn(*args)
+    with torch.cuda.device(device):
+        return fn(*args)
 
 
 def _on_gpu(device, **tensors):
@@ -56,8 +71,9 @@ def _on_gpu(device, **tensors):
     the library reads its pointer arguments as device memory."""
     if device.type != "cuda":
         raise ValueError(f"tensors must be on a GPU, got {device}")
+    idx = device.index
     for name, t in tensors.items():
-        if t is not None and t.device != device:
+        if t is not None and t.get_device() != idx:
             raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
@@ -66,37 +82,65 @@ def _ptr(t):
 
 
 def _i32_on(t, device):
-    """int32 device copy of a length / index tensor (no copy if already so)."""
-    if not isinstance(t, torch.Tensor):
+    """int32 contiguous device copy of a length / index tensor; the tensor
+    itself when it already is one."""
+    if isinstance(t, torch.Tensor):
+        if t.dtype == torch.int32 and t.get_device() == device.index and t.is_contiguous():
+            return t
+    else:
         t = torch.as_tensor(t)
     if t.dtype != torch.int32:
         t = t.to(torch.int32)
     return t.to(device).contiguous()
 
 
-def _split_cache(paged_kv_cache):
-    """(k, v, page_stride_k, page_stride_v) from a 5D tensor or a (k, v) tuple."""
-    if isinstance(paged_kv_cache, (tuple, list)):
-        k, v = paged_kv_cache
-    else:
-        if paged_kv_cache.dim() != 5 or paged_kv_cache.shape[1] != 2:
-            raise ValueError("a single paged_kv_cache tensor must be 5D with dim 1 == 2")
-        k, v = paged_kv_cache[:, 0], paged_kv_cache[:, 1]
-    for t in (k, v):
-        if t.dim() != 4:
-            raise ValueError("k/v caches must be 4D [pages, ., ., head_dim]")
-        inner = t.shape[1] * t.shape[2] * t.shape[3]
-        if (t.stride(3), t.stride(2), t.stride(1)) != (1, t.shape[3], t.shape[2] * t.shape[3]) \
-                or t.stride(0) < inner:
-            raise ValueError("each page of the k/v cache must be contiguous")
-    return k, v, k.stride(0), v.stride(0)
+class _Cache:
+    """Base pointers, page strides (elements) and dims of a paged K/V cache
+    given as a 5D tensor [pages, 2, ., ., head_dim] or a (k, v) pair of 4D
+    tensors [pages, ., ., head_dim]; each page must be contiguous."""
+
+    __slots__ = ("k_ptr", "v_ptr", "psk", "psv", "dims", "dtype", "device", "k_tensor",
+                 "v_tensor")
+
+    def __init__(self, paged_kv_cache):
+        if isinstance(paged_kv_cache, (tuple, list)):
+            k, v = paged_kv_cache
+            for t in (k, v):
+                if t.dim() != 4:
+                    raise ValueError("k/v caches must be 4D [pages, ., ., head_dim]")
+                _page_contiguous(t.shape[1:], t.stride())
+            self.k_ptr, self.v_ptr = k.data_ptr(), v.data_ptr()
+            self.psk, self.psv = k.stride(0), v.stride(0)
+            self.dims = tuple(k.shape[1:])
+            if v.dtype != k.dtype:
+                raise ValueError("k and v caches must share one dtype")
+            self.dtype, self.device = k.dtype, k.device
+            self.k_tensor, self.v_tensor = k, v
+        else:
+            c = paged_kv_cache
+            if c.dim() != 5 or c.shape[1] != 2:
+                raise ValueError("a single paged_kv_cache tensor must be 5D with dim 1 == 2")
+            st = c.stride()
+            _page_contiguous(c.shape[2:], (st[0],) + st[2:])
+            self.k_ptr = c.data_ptr()
+            self.v_ptr = self.k_ptr + st[1] * c.element_size()
+            self.psk = self.psv = st[0]
+            self.dims = tuple(c.shape[2:])
+            self.dtype, self.device = c.dtype, c.device
+            self.k_tensor = self.v_tensor = c
 
 
-def _cache_dims(k, layout):
-    """(page_size, num_kv_heads, head_dim) of a 4D cache view."""
+def _page_contiguous(inner_shape, strides):
+    a, b, d = inner_shape
+    if (strides[3], strides[2], strides[1]) != (1, d, b * d) or strides[0] < a * b * d:
+        raise ValueError("each page of the k/v cache must be contiguous")
+
+
+def _cache_dims(dims, layout):
+    """(page_size, num_kv_heads, head_dim) from a cache's per-page dims."""
     if layout == NHD:
-        return k.shape[1], k.shape[2], k.shape[3]
-    return k.shape[2], k.shape[1], k.shape[3]
+        return dims[0], dims[1], dims[2]
+    return dims[1], dims[0], dims[2]
 
 
 def get_seq_lens(kv_indptr, kv_last_page_len, page_size):
@@ -106,10 +150,8 @@ def get_seq_lens(kv_indptr, kv_last_page_len, page_size):
     indptr = _i32_on(kv_indptr, dev)
     last = _i32_on(kv_last_page_len, dev)
     out = torch.empty(last.shape[0], dtype=torch.int32, device=dev)
-    with torch.cuda.device(dev):
-        _lib.check(_lib.load().pkv_get_seq_lens(_ptr(indptr), _ptr(last), last.shape[0],
-                                                int(page_size), _ptr(out), _stream(dev)),
-                   "get_seq_lens")
+    _lib.check(_call(dev, _lib.load().pkv_get_seq_lens, _ptr(indptr), _ptr(last),
+                     last.shape[0], int(page_size), _ptr(out), _stream(dev)), "get_seq_lens")
     return out
 
 
@@ -122,10 +164,9 @@ def get_batch_indices_positions(append_indptr, seq_lens, nnz):
     seq = _i32_on(seq_lens, dev)
     bi = torch.empty(int(nnz), dtype=torch.int32, device=dev)
     pos = torch.empty(int(nnz), dtype=torch.int32, device=dev)
-    with torch.cuda.device(dev):
-        _lib.check(_lib.load().pkv_get_batch_indices_positions(
-            _ptr(ai), _ptr(seq), seq.shape[0], int(nnz), _ptr(bi), _ptr(pos), _stream(dev)),
-            "get_batch_indices_positions")
+    _lib.check(_call(dev, _lib.load().pkv_get_batch_indices_positions, _ptr(ai), _ptr(seq),
+                     seq.shape[0], int(nnz), _ptr(bi), _ptr(pos), _stream(dev)),
+               "get_batch_indices_positions")
     return bi, pos
 
 
@@ -138,10 +179,8 @@ def csr_to_block_tables(kv_indptr, kv_indices, max_pages_per_seq):
     idx = _i32_on(kv_indices, dev)
     batch = indptr.shape[0] - 1
     bt = torch.empty(batch, int(max_pages_per_seq), dtype=torch.int32, device=dev)
-    with torch.cuda.device(dev):
-        _lib.check(_lib.load().pkv_csr_to_block_tables(
-            _ptr(indptr), _ptr(idx), batch, int(max_pages_per_seq), _ptr(bt), _stream(dev)),
-            "csr_to_block_tables")
+    _lib.check(_call(dev, _lib.load().pkv_csr_to_block_tables, _ptr(indptr), _ptr(idx), batch,
+                     int(max_pages_per_seq), _ptr(bt), _stream(dev)), "csr_to_block_tables")
     return bt
 
 
@@ -150,22 +189,22 @@ def append_paged_kv_cache(append_key, append_value, batch_indices, positions,
                           kv_layout="NHD"):
     """Scatter appended K/V rows into their pages (in place; returns None)."""
     layout = _layout(kv_layout)
-    k, v, psk, psv = _split_cache(paged_kv_cache)
-    ps, hkv, d = _cache_dims(k, layout)
-    if append_key.dtype != k.dtype or append_value.dtype != k.dtype or v.dtype != k.dtype:
+    c = _Cache(paged_kv_cache)
+    ps, hkv, d = _cache_dims(c.dims, layout)
+    if append_key.dtype != c.dtype or append_value.dtype != c.dtype:
         raise ValueError("append rows and cache must share one dtype")
     if tuple(append_key.shape[1:]) != (hkv, d) or append_value.shape != append_key.shape:
         raise ValueError("append_key/append_value must be [nnz, num_kv_heads, head_dim]")
-    dev = k.device
-    _on_gpu(dev, v_cache=v, append_key=append_key, append_value=append_value)
+    dev = c.device
+    _on_gpu(dev, v_cache=c.v_tensor, append_key=append_key, append_value=append_value)
     ak, av = append_key.contiguous(), append_value.contiguous()
     bi, pos = _i32_on(batch_indices, dev), _i32_on(positions, dev)
     idx, indptr = _i32_on(kv_indices, dev), _i32_on(kv_indptr, dev)
-    with torch.cuda.device(dev):
-        _lib.check(_lib.load().pkv_append_paged_kv_cache(
-            _ptr(ak), _ptr(av), _ptr(bi), _ptr(pos), ak.shape[0], _ptr(k), _ptr(v), psk, psv,
-            _ptr(idx), _ptr(indptr), None, indptr.shape[0] - 1, hkv, d, ps, layout, _dt(k),
-            _stream(dev)), "append_paged_kv_cache")
+    _lib.check(_call(dev, _lib.load().pkv_append_paged_kv_cache, _ptr(ak), _ptr(av), _ptr(bi),
+                     _ptr(pos), ak.shape[0], c.k_ptr, c.v_ptr, c.psk, c.psv, _ptr(idx),
+                     _ptr(indptr), None, indptr.shape[0] - 1, hkv, d, ps, layout,
+                     _dt(ak), _stream(dev)),
+               "append_paged_kv_cache")
 
 
 def prefill_workspace_size(batch_size):
@@ -207,12 +246,12 @@ def batch_prefill_with_kv_cache(q, k_cache, v_cache, scale, workspace_buffer, *,
     paged = block_tables is not None
     if paged:
         layout = _layout(kv_layout)
-        ps, hkv, d_qk = _cache_dims(k_cache, layout)
-        _, _, d_vo = _cache_dims(v_cache, layout)
         for t in (k_cache, v_cache):
-            if t.dim() != 4 or t.stride(-1) != 1 or t.stride(-2) != t.shape[-1] or \
-                    t.stride(1) != t.shape[2] * t.shape[3]:
-                raise ValueError("each page of k_cache/v_cache must be contiguous")
+            if t.dim() != 4:
+                raise ValueError("paged k_cache/v_cache must be 4D [pages, ., ., d]")
+            _page_contiguous(t.shape[1:], t.stride())
+        ps, hkv, d_qk = _cache_dims(k_cache.shape[1:], layout)
+        _, _, d_vo = _cache_dims(v_cache.shape[1:], layout)
     else:
         layout, ps = NHD, 16
         for t in (k_cache, v_cache):
@@ -254,16 +293,16 @@ def batch_prefill_with_kv_cache(q, k_cache, v_cache, scale, workspace_buffer, *,
             raise ValueError("batch offsets must have batch_size entries")
     keep = []
     scales = [_scale_ptr(x, dev, keep) for x in (q_scale, k_scale, v_scale)]
-    with torch.cuda.device(dev):
-        _lib.check(_lib.load().pkv_batch_prefill_with_kv_cache(
-            _ptr(q), _ptr(k_cache), _ptr(v_cache), k_cache.stride(0) if paged else 0,
-            v_cache.stride(0) if paged else 0, float(scale), _ptr(workspace_buffer),
-            workspace_buffer.numel() * workspace_buffer.element_size(),
-            int(max_token_per_sequence), int(max_sequence_kv), _ptr(lq), _ptr(lkv),
-            _ptr(bt) if paged else None, bt.shape[1] if paged else 0, lq.shape[0], h_qo, hkv,
-            d_qk, d_vo, ps, layout, 1 if causal else 0, *scales, _ptr(out), _ptr(lse),
-            _dt(q), _dt(out), *[None if o is None else _ptr(o) for o in offs], _stream(dev)),
-            "batch_prefill_with_kv_cache")
+    _lib.check(_call(
+        dev, _lib.load().pkv_batch_prefill_with_kv_cache, _ptr(q), _ptr(k_cache),
+        _ptr(v_cache), k_cache.stride(0) if paged else 0, v_cache.stride(0) if paged else 0,
+        float(scale), _ptr(workspace_buffer),
+        workspace_buffer.numel() * workspace_buffer.element_size(),
+        int(max_token_per_sequence), int(max_sequence_kv), _ptr(lq), _ptr(lkv),
+        _ptr(bt) if paged else None, bt.shape[1] if paged else 0, lq.shape[0], h_qo, hkv,
+        d_qk, d_vo, ps, layout, 1 if causal else 0, *scales, _ptr(out), _ptr(lse),
+        _dt(q), _dt(out), *[None if o is None else _ptr(o) for o in offs], _stream(dev)),
+        "batch_prefill_with_kv_cache")
     return out, lse
 
 
@@ -290,8 +329,8 @@ def batch_decode_with_kv_cache(query, kv_cache, workspace_buffer, block_tables, 
     """
     layout = _layout(kv_layout)
     dev = query.device
-    k, v, psk, psv = _split_cache(kv_cache)
-    ps, hkv, d = _cache_dims(k, layout)
+    c = _Cache(kv_cache)
+    ps, hkv, d = _cache_dims(c.dims, layout)
     if query.dim() != 3 or query.shape[2] != d:
         raise ValueError("query must be [num_tokens, num_heads, head_dim]")
     query = query.contiguous()
@@ -312,7 +351,7 @@ def batch_decode_with_kv_cache(query, kv_cache, workspace_buffer, block_tables, 
     if mask is not None:
         if tuple(mask.shape) != (batch, q_max, q_max):
             raise ValueError("mask must be [batch_size, Q, Q] with Q the query count per request")
-        if mask.dtype not in (torch.bool, torch.uint8) or mask.device != dev \
+        if mask.dtype not in (torch.bool, torch.uint8) or mask.get_device() != dev.index \
                 or not mask.is_contiguous():
             raise ValueError("mask must be a contiguous bool or uint8 tensor on the "
                              "query's device")
@@ -323,32 +362,38 @@ def batch_decode_with_kv_cache(query, kv_cache, workspace_buffer, block_tables, 
         out = torch.empty(query.shape[0], h_qo, d, dtype=out_dtype, device=dev)
     if out.dtype != out_dtype or not out.is_contiguous() or tuple(out.shape) != tuple(query.shape):
         raise ValueError("out must be a contiguous tensor shaped like query")
-    _on_gpu(dev, k_cache=k, v_cache=v, workspace_buffer=workspace_buffer, out=out)
+    _on_gpu(dev, k_cache=c.k_tensor, v_cache=c.v_tensor, workspace_buffer=workspace_buffer,
+            out=out)
     bt = _i32_on(block_tables, dev)
-    seq = seq_lens.to(dev)
-    if seq.dtype not in (torch.int32, torch.uint32):
-        seq = seq.to(torch.int32)
-    seq = seq.contiguous()
+    seq = seq_lens
+    if not (isinstance(seq, torch.Tensor) and seq.dtype in (torch.int32, torch.uint32)
+            and seq.get_device() == dev.index and seq.is_contiguous()):
+        seq = torch.as_tensor(seq).to(dev)
+        if seq.dtype not in (torch.int32, torch.uint32):
+            seq = seq.to(torch.int32)
+        seq = seq.contiguous()
     if seq.shape[0] != batch:
         raise ValueError("seq_lens must have batch_size entries")
     sink_ptr = None
     if sinks is not None:
         if isinstance(sinks, (list, tuple)):
             sinks = torch.cat([s.reshape(-1) for s in sinks])
-        sinks = sinks.to(device=dev, dtype=torch.float32).contiguous()
+        if not (sinks.dtype == torch.float32 and sinks.get_device() == dev.index
+                and sinks.is_contiguous()):
+            sinks = sinks.to(device=dev, dtype=torch.float32).contiguous()
         if sinks.numel() != h_qo:
             raise ValueError("sinks must hold one value per qo head")
         sink_ptr = sinks.data_ptr()
     b1, b1_ptr = _scale_arg(bmm1_scale, dev, "bmm1_scale")
     b2, b2_ptr = _scale_arg(bmm2_scale, dev, "bmm2_scale")
-    with torch.cuda.device(dev):
-        _lib.check(_lib.load().pkv_batch_decode_with_kv_cache(
-            _ptr(query), _ptr(k), _ptr(v), psk, psv, _ptr(workspace_buffer),
-            workspace_buffer.numel() * workspace_buffer.element_size(), _ptr(bt), bt.shape[1],
-            _ptr(seq), batch, int(max_seq_len), b1, b2, int(window_left), _ptr(out), _dt(out),
-            sink_ptr, layout, int(q_len_per_req), h_qo, hkv, d, ps, _dt(query), _dt(k), b1_ptr,
-            b2_ptr, float(o_scale), None if cum is None else cum.data_ptr(),
-            0 if cum is None else q_max, mask_ptr, _stream(dev)), "batch_decode_with_kv_cache")
+    _lib.check(_call(
+        dev, _lib.load().pkv_batch_decode_with_kv_cache, _ptr(query), c.k_ptr, c.v_ptr, c.psk,
+        c.psv, _ptr(workspace_buffer), workspace_buffer.numel() * workspace_buffer.element_size(),
+        _ptr(bt), bt.shape[1], _ptr(seq), batch, int(max_seq_len), b1, b2, int(window_left),
+        _ptr(out), _dt(out), sink_ptr, layout, int(q_len_per_req), h_qo, hkv, d, ps, _dt(query),
+        _dtc(c.dtype), b1_ptr, b2_ptr, float(o_scale),
+        None if cum is None else cum.data_ptr(), 0 if cum is None else q_max, mask_ptr,
+        _stream(dev)), "batch_decode_with_kv_cache")
     return out
 
 
@@ -356,7 +401,7 @@ def _scale_arg(x, dev, name):
     """(host float, device pointer or None) for a float or a one-element
     float32 device tensor."""
     if isinstance(x, torch.Tensor):
-        if x.dtype != torch.float32 or x.numel() != 1 or x.device != dev:
+        if x.dtype != torch.float32 or x.numel() != 1 or x.get_device() != dev.index:
             raise ValueError(f"{name} tensor must be one float32 element on {dev}")
         return 1.0, x.data_ptr()
     return float(x), None

@@ -206,7 +206,25 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
   if (rows <= 0) return;
   const int lo = key_origin(a, seq, ql);
   const int k_begin = lo + split * chunk;
-  if (k_begin >= seq) return;
+  if (k_begin >= seq) {
+    // Only an empty sequence leaves split 0 without keys. Its rows see no
+    // key, so their output is zero; split 0 writes it (the merge kernel
+    // skips such rows), whatever the batch's split plan.
+    if (seq == 0 && split == 0) {
+      const int ob = a.out_dtype == 2 ? 1 : 2;  // bytes per output element
+      for (int idx = tid; idx < rows * (kD / 8); idx += kThreads) {
+        const int ng = row_base + idx / (kD / 8);
+        const int qi = ng / G, g = ng - qi * G;
+        const int64_t orow = (int64_t)(qrow0 + qi) * a.num_heads_qo + kvh * G + g;
+        char *op = (char *)a.out + (orow * kD + (idx % (kD / 8)) * 8) * ob;
+        if (ob == 2)
+          st16(op, u32x4{0u, 0u, 0u, 0u});
+        else
+          st8(op, u32x2{0u, 0u});
+      }
+    }
+    return;
+  }
   const int k_end = min(seq, k_begin + chunk);
   const int n_splits = (seq - lo + chunk - 1) / chunk;
   const int cw = chunk / kWaves;
@@ -609,7 +627,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a,
   const int qi = n / G, g = n - qi * G;
   const int head = kvh * G + g;
   const int64_t orow = (int64_t)(qrow0 + qi) * a.num_heads_qo + head;
-  if (n_splits == 1) return;  // written by the split kernel
+  if (n_splits <= 1) return;  // written by the split kernel (empty sequences too)
   const int64_t unit0 = ((int64_t)b * a.num_heads_kv + kvh) * max_splits;
   // One pass over the splits with a running maximum M (starting at the
   // sink logit), four splits' loads in flight at a time: L and O are

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import workloads
-from tests.helpers import assert_out_close, bits, oracle_decode
+from tests.helpers import assert_out_close, bits, fmt, oracle_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -20,7 +20,7 @@ def pkv():
     return m
 
 
-def run_decode(pkv, w, kv_cache=None):
+def run_decode(pkv, w, kv_cache=None, out_dtype=None):
     kv = w["kv_cache"] if kv_cache is None else kv_cache
     ws = torch.zeros(max(pkv.decode_workspace_size(
         w["seq_lens"].shape[0], w["q_len_per_req"], w["num_qo_heads"], w["num_kv_heads"],
@@ -29,7 +29,8 @@ def run_decode(pkv, w, kv_cache=None):
     out = pkv.batch_decode_with_kv_cache(
         w["query"], kv, ws, w["block_tables"].to(DEV), w["seq_lens"].to(DEV), w["max_seq_len"],
         bmm1_scale=w["bmm1_scale"], bmm2_scale=w["bmm2_scale"], window_left=w["window_left"],
-        sinks=sinks, kv_layout=w["layout"], q_len_per_req=w["q_len_per_req"])
+        sinks=sinks, kv_layout=w["layout"], q_len_per_req=w["q_len_per_req"],
+        out_dtype=out_dtype)
     torch.cuda.synchronize()
     return out
 
@@ -98,6 +99,85 @@ def test_rows_64(pkv):
 def test_seq_shorter_than_q_len(pkv):
     w = small(q_len_per_req=4, num_qo_heads=4, num_kv_heads=4, seed=44, batch=3, seq=(1, 3))
     check(pkv, w)
+
+
+# ---- fp16 queries, output types other than the query's, empty requests ------
+
+def _merged(pkv, w):
+    """True when a decode call's plan has several splits per (request, kv
+    head): partials go to the workspace and the merge kernel writes the
+    output. False: each unit writes its output directly."""
+    return (pkv.decode_workspace_size(w["seq_lens"].shape[0], w["q_len_per_req"],
+                                      w["num_qo_heads"], w["num_kv_heads"], 128,
+                                      w["max_seq_len"], w["window_left"]) > 0)
+
+
+@pytest.mark.parametrize("kv_dtype", [torch.float16, torch.float8_e4m3fn])
+@pytest.mark.parametrize("seq,window,seed,merged", [((1, 900), -1, 130, False),
+                                                    ((3000, 9000), 2500, 131, True)])
+def test_f16_query(pkv, kv_dtype, seq, window, seed, merged):
+    # an fp16 query over an fp16 or e4m3 cache (e4m3 widened exactly to
+    # fp16), fp16 output; short sequences take the direct write, long ones
+    # the split partials and the merge kernel
+    w = small(seed=seed, seq=seq, batch=4, q_len_per_req=2, window_left=window, sinks=True,
+              num_qo_heads=16, num_kv_heads=2, kv_dtype=kv_dtype, q_dtype=torch.float16,
+              page_size=32)
+    assert _merged(pkv, w) == merged
+    out = check(pkv, w)
+    assert out.dtype == torch.float16
+
+
+@pytest.mark.parametrize("q_dtype,kv_dtype,out_dtype", [
+    (torch.bfloat16, torch.bfloat16, torch.float16),
+    (torch.bfloat16, torch.float8_e4m3fn, torch.float16),
+    (torch.float16, torch.float16, torch.bfloat16),
+    (torch.float16, torch.float8_e4m3fn, torch.bfloat16),
+])
+@pytest.mark.parametrize("seq,seed,merged", [((1, 900), 132, False), ((3000, 9000), 133, True)])
+def test_output_dtype_other_than_query(pkv, q_dtype, kv_dtype, out_dtype, seq, seed, merged):
+    # out_dtype picks the output's 16-bit type independently of the query;
+    # both writers (direct and merge) round to it
+    w = small(seed=seed, seq=seq, batch=4, q_len_per_req=3, window_left=-1, sinks=True,
+              num_qo_heads=8, num_kv_heads=2, kv_dtype=kv_dtype, q_dtype=q_dtype)
+    assert _merged(pkv, w) == merged
+    out = run_decode(pkv, w, out_dtype=out_dtype)
+    assert out.dtype == out_dtype
+    err = assert_out_close(out, oracle_decode(w), out_dtype)
+    print(f"max |out err| {err:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("seq,out_dtype,merged", [((300, 900), torch.bfloat16, False),
+                                                  ((4000, 9000), torch.float16, True),
+                                                  ((300, 900), torch.float8_e4m3fn, False),
+                                                  ((4000, 9000), torch.float8_e4m3fn, True)])
+def test_zero_length_request(pkv, seq, out_dtype, merged):
+    # a request whose sequence is empty: its query rows see no key and come
+    # back zero, whether the batch's plan writes outputs directly (one
+    # split) or through the merge kernel; the other requests are unaffected
+    w = small(seed=134, batch=4, seq=seq, q_len_per_req=2, sinks=True, num_qo_heads=8,
+              num_kv_heads=2, window_left=-1)
+    sl = w["seq_lens"].to(torch.int64)
+    sl[1] = 0
+    w = dict(w, seq_lens=sl.to(torch.uint32))
+    assert _merged(pkv, w) == merged
+    ws = torch.zeros(max(pkv.decode_workspace_size(4, 2, 8, 2, 128, w["max_seq_len"], -1), 16),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.full(w["query"].shape, float("nan"), dtype=torch.float32,
+                     device=DEV).to(out_dtype)
+    pkv.batch_decode_with_kv_cache(
+        w["query"], w["kv_cache"], ws, w["block_tables"].to(DEV), w["seq_lens"].to(DEV),
+        w["max_seq_len"], bmm1_scale=w["bmm1_scale"], bmm2_scale=w["bmm2_scale"],
+        sinks=w["sinks"].to(DEV), kv_layout=w["layout"], q_len_per_req=2, out=out,
+        out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    if out_dtype == torch.float8_e4m3fn:
+        raw = out.view(torch.uint8)
+        assert torch.all((raw[2:4] & 0x7F) == 0), "empty request's rows must be zero"
+        ref = oracle_decode(w)
+        check_fp8_out(out, ref, 1.0)
+    else:
+        assert torch.all(out[2:4].float() == 0), "empty request's rows must be zero"
+        assert_out_close(out, oracle_decode(w), out_dtype)
 
 
 def test_e4m3_decode_table_exhaustive(pkv):
@@ -315,8 +395,7 @@ def oracle_decode_ragged(w, cum, mask=None):
     sub, bt = compact_pages(w["kv_cache"], w["block_tables"], used)
     sinks = None if w["sinks"] is None else w["sinks"].double().numpy()
     return oracle.batch_decode(
-        bits(w["query"]), oracle.formats.BF16, bits(sub[:, 0]), bits(sub[:, 1]),
-        oracle.formats.E4M3 if w["kv_cache"].dtype == torch.float8_e4m3fn else oracle.formats.BF16,
+        bits(w["query"]), fmt(w["query"]), bits(sub[:, 0]), bits(sub[:, 1]), fmt(w["kv_cache"]),
         bt.numpy(), seq.numpy(), w["bmm1_scale"], w["bmm2_scale"], w["window_left"], sinks,
         w["layout"], cum_seq_lens_q=cum, spec_mask=None if mask is None else mask.cpu().numpy())
 

@@ -117,6 +117,22 @@ def test_fp8_d128_fp16_out(pkv):
     check(pkv, w, o_dtype=torch.float16)
 
 
+@pytest.mark.parametrize("dtype,o_dtype", [(torch.float16, torch.bfloat16),
+                                            (torch.bfloat16, torch.float16)])
+@pytest.mark.parametrize("d_qk", [128, 192])
+def test_output_dtype_other_than_input(pkv, dtype, o_dtype, d_qk):
+    # o_data_type picks the output's 16-bit type independently of q/k/v
+    w = small_prefill(seed=15 + d_qk, dtype=dtype, d_qk=d_qk, num_qo_heads=8, num_kv_heads=2)
+    out, _ = check(pkv, w, o_dtype)
+    assert out.dtype == o_dtype
+
+
+def test_fp8_d192_fp16_out(pkv):
+    w = workloads.fp8_prefill(DEV, seed=16, batch=2, seq_len=290, num_heads=4)
+    out, _ = check(pkv, w, o_dtype=torch.float16)
+    assert out.dtype == torch.float16
+
+
 def test_edge_lengths(pkv):
     # L_q = 1, L_kv < L_q (leading rows see no key), and an empty request
     w = small_prefill(seed=11, batch=4, q_len=(300, 300), prefix=(0, 0),

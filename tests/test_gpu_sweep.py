@@ -6,8 +6,10 @@ prefill), fp16/bf16/e4m3, window -1/0/7/100, sinks on or off and 1-4 queries
 per request (for decode). Two more sweeps cross the decode extensions
 (ragged query counts, random or tree draft masks, e4m3 output, device-tensor
 scales) and unpaged prefill with every batch offset in a random order with
-gaps. The per-dimension tests pin each feature alone; the sweeps cross them
-at random.
+gaps. A last sweep crosses the element types: prefill inputs fp16/bf16/e4m3
+with fp16 or bf16 output, decode queries fp16 or bf16 over K/V of the
+query's type or e4m3 with fp16/bf16/e4m3 output. The per-dimension tests pin
+each feature alone; the sweeps cross them at random.
 """
 
 import numpy as np
@@ -217,3 +219,64 @@ def test_prefill_unpaged_offsets_sweep(pkv, case):
         close_lse(lse[torch.from_numpy(wl).to(DEV)], ref_l[wl])
     assert torch.isnan(out[torch.from_numpy(~wo).to(DEV)].float()).all()
     assert torch.isnan(lse[torch.from_numpy(~wl).to(DEV)]).all()
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_dtype_sweep(pkv, case):
+    # input and output element types crossed at random, each case drawing a
+    # prefill and a decode: prefill q/k/v fp16, bf16 or e4m3 with fp16 or
+    # bf16 output; decode query fp16 or bf16, K/V the query's type or e4m3,
+    # output fp16, bf16 or e4m3; lengths long enough for split-KV merges
+    from tests.test_gpu_decode import check_fp8_out
+    rng = np.random.default_rng(5000 + case)
+    dtype = _pick(rng, [torch.float16, torch.bfloat16, torch.float8_e4m3fn])
+    o_dtype = _pick(rng, [torch.float16, torch.bfloat16])
+    hkv = _pick(rng, [1, 2])
+    G = _pick(rng, [1, 4, 8])
+    d_qk = _pick(rng, [128, 192])
+    B = int(rng.integers(1, 5))
+    kw = dict(batch=B, q_len=(1, int(rng.integers(1, 260))), prefix=(0, 200),
+              num_qo_heads=hkv * G, num_kv_heads=hkv, d_qk=d_qk,
+              page_size=_pick(rng, [16, 32, 64]), layout=_pick(rng, ["NHD", "HND"]),
+              pool_pages=B * (500 // 16 + 2) + 5)
+    if dtype == torch.float8_e4m3fn:
+        w = workloads.batch_prefill(DEV, seed=5000 + case, dtype=torch.bfloat16, **kw)
+        for key in ("q", "k_cache", "v_cache"):
+            w[key] = w[key].to(torch.float8_e4m3fn)
+        sc = rng.uniform(0.5, 2.0, 3)
+        w["q_scale"], w["k_scale"], w["v_scale"] = (
+            torch.tensor([float(x)], dtype=torch.float32) for x in sc)
+    else:
+        w = workloads.batch_prefill(DEV, seed=5000 + case, dtype=dtype, **kw)
+    print(f"case {case} prefill: {dtype} -> {o_dtype} B {B} G {G} hkv {hkv} d_qk {d_qk} "
+          f"lq {w['seq_lens_q'].tolist()} lkv {w['seq_lens_kv'].tolist()}", flush=True)
+    out, lse = run_prefill(pkv, w, o_dtype)
+    assert out.dtype == o_dtype
+    ref_o, ref_l = oracle_prefill(w)
+    assert_out_close(out, ref_o, o_dtype)
+    assert_lse_close(lse, ref_l)
+
+    q_dtype = _pick(rng, [torch.float16, torch.bfloat16])
+    kv_dtype = _pick(rng, [q_dtype, torch.float8_e4m3fn])
+    d_out = _pick(rng, [torch.float16, torch.bfloat16, torch.float8_e4m3fn])
+    ql = int(rng.integers(1, 5))
+    Gd = _pick(rng, [g for g in (1, 2, 4, 8, 16) if g * ql <= 64])
+    window = _pick(rng, [-1, 7, 1500])
+    w = workloads.batch_decode(DEV, seed=6000 + case, batch=int(rng.integers(1, 7)),
+                               seq=(1, int(rng.integers(1, 6001))), num_qo_heads=hkv * Gd,
+                               num_kv_heads=hkv, q_len_per_req=ql,
+                               page_size=_pick(rng, [16, 32, 64]),
+                               layout=_pick(rng, ["NHD", "HND"]), kv_dtype=kv_dtype,
+                               q_dtype=q_dtype, window_left=window,
+                               sinks=bool(rng.integers(0, 2)))
+    w["bmm2_scale"] = float(rng.uniform(0.5, 2.0))
+    print(f"case {case} decode: q {q_dtype} kv {kv_dtype} out {d_out} G {Gd} hkv {hkv} ql {ql} "
+          f"ps {w['page_size']} {w['layout']} window {window} seq {w['seq_lens'].tolist()}",
+          flush=True)
+    got = run_decode(pkv, w, out_dtype=d_out)
+    assert got.dtype == d_out
+    ref = oracle_decode(w)
+    if d_out == torch.float8_e4m3fn:
+        check_fp8_out(got, ref, 1.0)
+    else:
+        assert_out_close(got, ref, d_out)

@@ -125,17 +125,19 @@ def fp8_prefill(device="cpu", seed=3, batch=8, seq_len=4096, num_heads=16, d_qk=
 
 def batch_decode(device="cpu", seed=4, batch=256, seq=(512, 8192), num_qo_heads=32,
                  num_kv_heads=8, head_dim=128, page_size=16, q_len_per_req=1,
-                 kv_dtype=torch.bfloat16, layout=HND, window_left=-1, sinks=False):
+                 kv_dtype=torch.bfloat16, layout=HND, window_left=-1, sinks=False,
+                 q_dtype=torch.bfloat16):
     """Batch decode over block_tables: seq_lens uint32 ~ U{seq}, HND page 16,
     random page order, bf16 K/V and query ~ N(0,1), bmm1 = 1/sqrt(128),
-    bmm2 = 1, window -1, one query per request."""
+    bmm2 = 1, window -1, one query per request. ``q_dtype`` (bf16 or fp16)
+    is the query's type; a 16-bit ``kv_dtype`` must match it."""
     host, dev = _gens(seed, device)
     sl = _uniform_int(host, seq[0], seq[1], batch).to(torch.int64)
     bt, pool = _page_tables(sl.tolist(), page_size, None, host)
     shape = (pool, 2, num_kv_heads, page_size, head_dim) if layout == HND \
         else (pool, 2, page_size, num_kv_heads, head_dim)
     kv = _randn(shape, dev, device, kv_dtype)
-    q = _randn((batch * q_len_per_req, num_qo_heads, head_dim), dev, device, torch.bfloat16)
+    q = _randn((batch * q_len_per_req, num_qo_heads, head_dim), dev, device, q_dtype)
     sk = None
     if sinks:
         sk = torch.randn(num_qo_heads, generator=host).to(torch.float32)
