@@ -24,6 +24,7 @@ __all__ = [
     "append_paged_kv_cache",
     "batch_prefill_with_kv_cache",
     "batch_decode_with_kv_cache",
+    "batch_decode_with_kv_cache_no_alloc",
     "prefill_workspace_size",
     "decode_workspace_size",
     "PkvError",
@@ -327,6 +328,29 @@ def batch_decode_with_kv_cache(query, kv_cache, workspace_buffer, block_tables, 
     own query count; mask ([batch, Q, Q] bool or uint8) lets draft t see
     draft i when mask[b, t, i] is set, in place of the causal rule.
     """
+    return _decode(False, query, kv_cache, workspace_buffer, block_tables, seq_lens,
+                   max_seq_len, bmm1_scale, bmm2_scale, window_left, out, out_dtype, sinks,
+                   kv_layout, q_len_per_req, o_scale, mask, max_q_len, cum_seq_lens_q)
+
+
+def batch_decode_with_kv_cache_no_alloc(query, kv_cache, block_tables, seq_lens, max_seq_len,
+                                        *, out, bmm1_scale=1.0, bmm2_scale=1.0, window_left=-1,
+                                        sinks=None, kv_layout="HND", q_len_per_req=1,
+                                        o_scale=1.0, mask=None, max_q_len=None,
+                                        cum_seq_lens_q=None):
+    """batch_decode_with_kv_cache without a workspace, for callers that cannot
+    allocate: the split partials go to the library's static scratch array
+    (64 MiB per GPU; larger split plans raise ValueError). ``out`` is
+    required and its dtype is the output type. Calls that overlap on one GPU
+    share that array and race: serialise them."""
+    return _decode(True, query, kv_cache, None, block_tables, seq_lens, max_seq_len,
+                   bmm1_scale, bmm2_scale, window_left, out, out.dtype, sinks, kv_layout,
+                   q_len_per_req, o_scale, mask, max_q_len, cum_seq_lens_q)
+
+
+def _decode(no_alloc, query, kv_cache, workspace_buffer, block_tables, seq_lens, max_seq_len,
+            bmm1_scale, bmm2_scale, window_left, out, out_dtype, sinks, kv_layout,
+            q_len_per_req, o_scale, mask, max_q_len, cum_seq_lens_q):
     layout = _layout(kv_layout)
     dev = query.device
     c = _Cache(kv_cache)
@@ -386,14 +410,19 @@ def batch_decode_with_kv_cache(query, kv_cache, workspace_buffer, block_tables, 
         sink_ptr = sinks.data_ptr()
     b1, b1_ptr = _scale_arg(bmm1_scale, dev, "bmm1_scale")
     b2, b2_ptr = _scale_arg(bmm2_scale, dev, "bmm2_scale")
+    lib = _lib.load()
+    if no_alloc:
+        fn, name, ws = lib.pkv_batch_decode_with_kv_cache_no_alloc, \
+            "batch_decode_with_kv_cache_no_alloc", ()
+    else:
+        fn, name = lib.pkv_batch_decode_with_kv_cache, "batch_decode_with_kv_cache"
+        ws = (_ptr(workspace_buffer), workspace_buffer.numel() * workspace_buffer.element_size())
     _lib.check(_call(
-        dev, _lib.load().pkv_batch_decode_with_kv_cache, _ptr(query), c.k_ptr, c.v_ptr, c.psk,
-        c.psv, _ptr(workspace_buffer), workspace_buffer.numel() * workspace_buffer.element_size(),
-        _ptr(bt), bt.shape[1], _ptr(seq), batch, int(max_seq_len), b1, b2, int(window_left),
-        _ptr(out), _dt(out), sink_ptr, layout, int(q_len_per_req), h_qo, hkv, d, ps, _dt(query),
-        _dtc(c.dtype), b1_ptr, b2_ptr, float(o_scale),
-        None if cum is None else cum.data_ptr(), 0 if cum is None else q_max, mask_ptr,
-        _stream(dev)), "batch_decode_with_kv_cache")
+        dev, fn, _ptr(query), c.k_ptr, c.v_ptr, c.psk, c.psv, *ws, _ptr(bt), bt.shape[1],
+        _ptr(seq), batch, int(max_seq_len), b1, b2, int(window_left), _ptr(out), _dt(out),
+        sink_ptr, layout, int(q_len_per_req), h_qo, hkv, d, ps, _dt(query), _dtc(c.dtype),
+        b1_ptr, b2_ptr, float(o_scale), None if cum is None else cum.data_ptr(),
+        0 if cum is None else q_max, mask_ptr, _stream(dev)), name)
     return out
 
 

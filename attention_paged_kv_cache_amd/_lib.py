@@ -49,7 +49,14 @@ SIGNATURES = {
         _P, _P, _P, _I64, _I64, _P, _SZ, _P, _I32, _P, _I32, _I32, _F, _F, _I32,
         _P, ctypes.c_int, _P, ctypes.c_int, _I32, _I32, _I32, _I32, _I32,
         ctypes.c_int, ctypes.c_int, _P, _P, _F, _P, _I32, _P, _P]),
+    "pkv_batch_decode_with_kv_cache_no_alloc": (ctypes.c_int, [
+        _P, _P, _P, _I64, _I64, _P, _I32, _P, _I32, _I32, _F, _F, _I32,
+        _P, ctypes.c_int, _P, ctypes.c_int, _I32, _I32, _I32, _I32, _I32,
+        ctypes.c_int, ctypes.c_int, _P, _P, _F, _P, _I32, _P, _P]),
 }
+
+# bytes of the no-alloc decode's static scratch array (PKV_DECODE_SCRATCH_BYTES)
+DECODE_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 

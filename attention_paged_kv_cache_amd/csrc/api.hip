@@ -3,12 +3,15 @@
 // Every entry point checks its host-side arguments first and returns an
 // error before any HIP call if one is out of range, so the checks run (and
 // can be tested) on a machine without a GPU. The library never allocates,
-// never synchronises and never reads device memory on the host.
+// never synchronises and never reads device memory on the host. The
+// no-alloc decode entry point uses a static device array of the library's
+// own (at the end of this file) instead of a workspace.
 
 #include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -306,69 +309,132 @@ PKV_API size_t pkv_decode_workspace_size(int32_t batch_size,
       .workspace_bytes;
 }
 
-PKV_API pkv_status pkv_batch_decode_with_kv_cache(
-    const void *query, const void *k_cache, const void *v_cache,
-    int64_t page_stride_k, int64_t page_stride_v, void *workspace,
-    size_t workspace_bytes, const int32_t *block_tables,
-    int32_t max_pages_per_seq, const uint32_t *seq_lens, int32_t batch_size,
-    int32_t max_seq_len, float bmm1_scale, float bmm2_scale,
-    int32_t window_left, void *out, pkv_dtype out_dtype, const float *sinks,
-    pkv_layout kv_layout, int32_t q_len_per_req, int32_t num_heads_qo,
-    int32_t num_heads_kv, int32_t head_dim, int32_t page_size,
-    pkv_dtype q_dtype, pkv_dtype kv_dtype, const float *bmm1_scale_dev,
-    const float *bmm2_scale_dev, float o_scale, const int32_t *cum_seq_lens_q,
-    int32_t max_q_len, const uint8_t *spec_mask, void *stream) {
-  CHECK(batch_size >= 0, PKV_ERR_INVALID_ARG, "batch_size < 0");
-  CHECK(q_len_per_req >= 1, PKV_ERR_INVALID_ARG, "q_len_per_req < 1");
-  CHECK(cum_seq_lens_q ? max_q_len >= 1 : max_q_len == 0, PKV_ERR_INVALID_ARG,
-        "max_q_len must be >= 1 with cum_seq_lens_q and 0 without it");
+// ---- decode ---------------------------------------------------------------
+//
+// The no-alloc entry point's split partials live in this file-scope device
+// array instead of a caller's workspace. Host code never uses the array's
+// name as an address: on the host it is only a stand-in for the symbol. The
+// device address comes from hipGetSymbolAddress, taken once per device (on
+// the first call that needs it on that device, with the device current) and
+// kept in g_scratch_addr.
+static __device__ __align__(256) char scratch[PKV_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device `stream` runs on, which must be
+// the current device.
+pkv_status scratch_address(hipStream_t stream, void **addr, const char *fn) {
+  int cur = -1, sdev = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return from_hip(e, fn);
+  e = hipStreamGetDevice(stream, &sdev);
+  if (e != hipSuccess) return from_hip(e, fn);
+  if (sdev != cur)
+    return fail(PKV_ERR_INVALID_ARG, fn, "the stream's device must be the current device");
+  if (cur < 0 || cur >= kMaxDevices)
+    return fail(PKV_ERR_UNSUPPORTED, fn, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[cur]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return from_hip(e, fn);
+    if (!p) return fail(PKV_ERR_HIP, fn, "hipGetSymbolAddress gave a null address");
+    g_scratch_addr[cur] = p;
+  }
+  *addr = g_scratch_addr[cur];
+  return PKV_OK;
+}
+
+#define CHECKF(cond, st, msg)                 \
+  do {                                        \
+    if (!(cond)) return fail((st), fn, (msg)); \
+  } while (0)
+
+// Both decode entry points: every argument check on host scalars first,
+// then (no-alloc only) the scratch array's address, then the launch.
+pkv_status decode_entry(
+    const char *fn, bool use_scratch, const void *query, const void *k_cache,
+    const void *v_cache, int64_t page_stride_k, int64_t page_stride_v, void *workspace,
+    size_t workspace_bytes, const int32_t *block_tables, int32_t max_pages_per_seq,
+    const uint32_t *seq_lens, int32_t batch_size, int32_t max_seq_len, float bmm1_scale,
+    float bmm2_scale, int32_t window_left, void *out, pkv_dtype out_dtype,
+    const float *sinks, pkv_layout kv_layout, int32_t q_len_per_req, int32_t num_heads_qo,
+    int32_t num_heads_kv, int32_t head_dim, int32_t page_size, pkv_dtype q_dtype,
+    pkv_dtype kv_dtype, const float *bmm1_scale_dev, const float *bmm2_scale_dev,
+    float o_scale, const int32_t *cum_seq_lens_q, int32_t max_q_len,
+    const uint8_t *spec_mask, void *stream) {
+  CHECKF(batch_size >= 0, PKV_ERR_INVALID_ARG, "batch_size < 0");
+  CHECKF(q_len_per_req >= 1, PKV_ERR_INVALID_ARG, "q_len_per_req < 1");
+  CHECKF(cum_seq_lens_q ? max_q_len >= 1 : max_q_len == 0, PKV_ERR_INVALID_ARG,
+         "max_q_len must be >= 1 with cum_seq_lens_q and 0 without it");
   // queries per request, or their maximum with variable-length queries
   const int32_t q_max = cum_seq_lens_q ? max_q_len : q_len_per_req;
-  CHECK(window_left >= -1, PKV_ERR_INVALID_ARG, "window_left < -1");
-  CHECK(num_heads_kv > 0 && num_heads_qo > 0, PKV_ERR_INVALID_ARG,
-        "head counts must be positive");
-  CHECK(num_heads_qo >= num_heads_kv, PKV_ERR_INVALID_ARG,
-        "num_heads_qo must be >= num_heads_kv");
-  CHECK(num_heads_qo % num_heads_kv == 0, PKV_ERR_UNSUPPORTED,
-        "num_heads_qo must be a multiple of num_heads_kv");
-  CHECK(head_dim == 128, PKV_ERR_UNSUPPORTED, "head_dim must be 128");
-  CHECK((int64_t)q_max * (num_heads_qo / num_heads_kv) <= 64, PKV_ERR_UNSUPPORTED,
-        "q_len_per_req (or max_q_len) * num_heads_qo / num_heads_kv must be <= 64");
-  CHECK(kv_layout == PKV_NHD || kv_layout == PKV_HND, PKV_ERR_INVALID_ARG,
-        "kv_layout must be NHD or HND");
-  CHECK(q_dtype == PKV_F16 || q_dtype == PKV_BF16, PKV_ERR_UNSUPPORTED,
-        "query dtype must be F16 or BF16");
-  CHECK(kv_dtype == q_dtype || kv_dtype == PKV_E4M3, PKV_ERR_UNSUPPORTED,
-        "kv dtype must equal the query dtype or be E4M3");
-  CHECK(out_dtype == PKV_F16 || out_dtype == PKV_BF16 || out_dtype == PKV_E4M3,
-        PKV_ERR_UNSUPPORTED, "output dtype must be F16, BF16 or E4M3");
-  CHECK(out_dtype != PKV_E4M3 || (o_scale > 0.0f && o_scale <= 3.4e38f),
-        PKV_ERR_INVALID_ARG, "o_scale must be finite and > 0");
-  CHECK(page_size_ok(page_size), PKV_ERR_UNSUPPORTED,
-        "page_size must be 16, 32 or 64");
-  CHECK(max_seq_len >= 0, PKV_ERR_INVALID_ARG, "max_seq_len < 0");
-  CHECK(max_pages_per_seq > 0, PKV_ERR_INVALID_ARG, "max_pages_per_seq <= 0");
-  CHECK((int64_t)max_pages_per_seq * page_size >= max_seq_len,
-        PKV_ERR_INVALID_ARG, "block_tables too narrow for max_seq_len");
+  CHECKF(window_left >= -1, PKV_ERR_INVALID_ARG, "window_left < -1");
+  CHECKF(num_heads_kv > 0 && num_heads_qo > 0, PKV_ERR_INVALID_ARG,
+         "head counts must be positive");
+  CHECKF(num_heads_qo >= num_heads_kv, PKV_ERR_INVALID_ARG,
+         "num_heads_qo must be >= num_heads_kv");
+  CHECKF(num_heads_qo % num_heads_kv == 0, PKV_ERR_UNSUPPORTED,
+         "num_heads_qo must be a multiple of num_heads_kv");
+  CHECKF(head_dim == 128, PKV_ERR_UNSUPPORTED, "head_dim must be 128");
+  CHECKF((int64_t)q_max * (num_heads_qo / num_heads_kv) <= 64, PKV_ERR_UNSUPPORTED,
+         "q_len_per_req (or max_q_len) * num_heads_qo / num_heads_kv must be <= 64");
+  CHECKF(kv_layout == PKV_NHD || kv_layout == PKV_HND, PKV_ERR_INVALID_ARG,
+         "kv_layout must be NHD or HND");
+  CHECKF(q_dtype == PKV_F16 || q_dtype == PKV_BF16, PKV_ERR_UNSUPPORTED,
+         "query dtype must be F16 or BF16");
+  CHECKF(kv_dtype == q_dtype || kv_dtype == PKV_E4M3, PKV_ERR_UNSUPPORTED,
+         "kv dtype must equal the query dtype or be E4M3");
+  CHECKF(out_dtype == PKV_F16 || out_dtype == PKV_BF16 || out_dtype == PKV_E4M3,
+         PKV_ERR_UNSUPPORTED, "output dtype must be F16, BF16 or E4M3");
+  CHECKF(out_dtype != PKV_E4M3 || (o_scale > 0.0f && o_scale <= 3.4e38f),
+         PKV_ERR_INVALID_ARG, "o_scale must be finite and > 0");
+  CHECKF(page_size_ok(page_size), PKV_ERR_UNSUPPORTED, "page_size must be 16, 32 or 64");
+  CHECKF(max_seq_len >= 0, PKV_ERR_INVALID_ARG, "max_seq_len < 0");
+  CHECKF(max_pages_per_seq > 0, PKV_ERR_INVALID_ARG, "max_pages_per_seq <= 0");
+  CHECKF((int64_t)max_pages_per_seq * page_size >= max_seq_len, PKV_ERR_INVALID_ARG,
+         "block_tables too narrow for max_seq_len");
   const int es = elem_bytes(kv_dtype);
   const int64_t pe = (int64_t)page_size * num_heads_kv * head_dim;
-  CHECK(page_stride_k >= pe && page_stride_v >= pe, PKV_ERR_INVALID_ARG,
-        "page stride smaller than one page");
-  CHECK((page_stride_k * es) % 16 == 0 && (page_stride_v * es) % 16 == 0,
-        PKV_ERR_UNSUPPORTED, "page strides must be multiples of 16 bytes");
+  CHECKF(page_stride_k >= pe && page_stride_v >= pe, PKV_ERR_INVALID_ARG,
+         "page stride smaller than one page");
+  CHECKF((page_stride_k * es) % 16 == 0 && (page_stride_v * es) % 16 == 0,
+         PKV_ERR_UNSUPPORTED, "page strides must be multiples of 16 bytes");
   const pkv::DecodePlan plan =
-      pkv::plan_decode(batch_size, q_max, num_heads_qo, num_heads_kv,
-                       head_dim, max_seq_len, window_left);
-  CHECK(workspace_bytes >= plan.workspace_bytes, PKV_ERR_WORKSPACE_TOO_SMALL,
-        "workspace smaller than pkv_decode_workspace_size(...)");
+      pkv::plan_decode(batch_size, q_max, num_heads_qo, num_heads_kv, head_dim,
+                       max_seq_len, window_left);
+  if (use_scratch) {
+    if (plan.workspace_bytes > PKV_DECODE_SCRATCH_BYTES) {
+      char msg[192];
+      snprintf(msg, sizeof msg,
+               "the split plan needs %zu bytes of workspace; the static scratch holds %zu "
+               "(use pkv_batch_decode_with_kv_cache with a workspace)",
+               plan.workspace_bytes, (size_t)PKV_DECODE_SCRATCH_BYTES);
+      return fail(PKV_ERR_WORKSPACE_TOO_SMALL, fn, msg);
+    }
+  } else {
+    CHECKF(workspace_bytes >= plan.workspace_bytes, PKV_ERR_WORKSPACE_TOO_SMALL,
+           "workspace smaller than pkv_decode_workspace_size(...)");
+  }
   if (batch_size == 0) return PKV_OK;
-  CHECK(query && k_cache && v_cache && block_tables && seq_lens && out,
-        PKV_ERR_INVALID_ARG, "null pointer");
-  CHECK(plan.workspace_bytes == 0 || workspace, PKV_ERR_INVALID_ARG,
-        "null workspace");
-  CHECK(aligned(query, 16) && aligned(k_cache, 16) && aligned(v_cache, 16) &&
-            aligned(out, 16) && aligned(workspace, 16),
-        PKV_ERR_UNSUPPORTED, "query/k/v/out/workspace must be 16-byte aligned");
+  CHECKF(query && k_cache && v_cache && block_tables && seq_lens && out,
+         PKV_ERR_INVALID_ARG, "null pointer");
+  CHECKF(use_scratch || plan.workspace_bytes == 0 || workspace, PKV_ERR_INVALID_ARG,
+         "null workspace");
+  CHECKF(aligned(query, 16) && aligned(k_cache, 16) && aligned(v_cache, 16) &&
+             aligned(out, 16) && aligned(workspace, 16),
+         PKV_ERR_UNSUPPORTED, "query/k/v/out/workspace must be 16-byte aligned");
+  if (use_scratch) {
+    workspace = nullptr;
+    if (plan.workspace_bytes > 0) {
+      const pkv_status st = scratch_address(as_stream(stream), &workspace, fn);
+      if (st != PKV_OK) return st;
+    }
+  }
 
   pkv::DecodeArgs a{};
   a.q = query;
@@ -407,5 +473,48 @@ PKV_API pkv_status pkv_batch_decode_with_kv_cache(
   a.kv_dtype = kv_dtype;
   a.out_dtype = out_dtype;
   a.workspace = workspace;
-  return from_hip(pkv::launch_decode(a, plan, as_stream(stream)), __func__);
+  return from_hip(pkv::launch_decode(a, plan, as_stream(stream)), fn);
+}
+
+#undef CHECKF
+
+}  // namespace
+
+PKV_API pkv_status pkv_batch_decode_with_kv_cache(
+    const void *query, const void *k_cache, const void *v_cache,
+    int64_t page_stride_k, int64_t page_stride_v, void *workspace,
+    size_t workspace_bytes, const int32_t *block_tables,
+    int32_t max_pages_per_seq, const uint32_t *seq_lens, int32_t batch_size,
+    int32_t max_seq_len, float bmm1_scale, float bmm2_scale,
+    int32_t window_left, void *out, pkv_dtype out_dtype, const float *sinks,
+    pkv_layout kv_layout, int32_t q_len_per_req, int32_t num_heads_qo,
+    int32_t num_heads_kv, int32_t head_dim, int32_t page_size,
+    pkv_dtype q_dtype, pkv_dtype kv_dtype, const float *bmm1_scale_dev,
+    const float *bmm2_scale_dev, float o_scale, const int32_t *cum_seq_lens_q,
+    int32_t max_q_len, const uint8_t *spec_mask, void *stream) {
+  return decode_entry(__func__, false, query, k_cache, v_cache, page_stride_k, page_stride_v,
+                      workspace, workspace_bytes, block_tables, max_pages_per_seq, seq_lens,
+                      batch_size, max_seq_len, bmm1_scale, bmm2_scale, window_left, out,
+                      out_dtype, sinks, kv_layout, q_len_per_req, num_heads_qo, num_heads_kv,
+                      head_dim, page_size, q_dtype, kv_dtype, bmm1_scale_dev, bmm2_scale_dev,
+                      o_scale, cum_seq_lens_q, max_q_len, spec_mask, stream);
+}
+
+PKV_API pkv_status pkv_batch_decode_with_kv_cache_no_alloc(
+    const void *query, const void *k_cache, const void *v_cache,
+    int64_t page_stride_k, int64_t page_stride_v, const int32_t *block_tables,
+    int32_t max_pages_per_seq, const uint32_t *seq_lens, int32_t batch_size,
+    int32_t max_seq_len, float bmm1_scale, float bmm2_scale,
+    int32_t window_left, void *out, pkv_dtype out_dtype, const float *sinks,
+    pkv_layout kv_layout, int32_t q_len_per_req, int32_t num_heads_qo,
+    int32_t num_heads_kv, int32_t head_dim, int32_t page_size,
+    pkv_dtype q_dtype, pkv_dtype kv_dtype, const float *bmm1_scale_dev,
+    const float *bmm2_scale_dev, float o_scale, const int32_t *cum_seq_lens_q,
+    int32_t max_q_len, const uint8_t *spec_mask, void *stream) {
+  return decode_entry(__func__, true, query, k_cache, v_cache, page_stride_k, page_stride_v,
+                      nullptr, 0, block_tables, max_pages_per_seq, seq_lens, batch_size,
+                      max_seq_len, bmm1_scale, bmm2_scale, window_left, out, out_dtype, sinks,
+                      kv_layout, q_len_per_req, num_heads_qo, num_heads_kv, head_dim,
+                      page_size, q_dtype, kv_dtype, bmm1_scale_dev, bmm2_scale_dev, o_scale,
+                      cum_seq_lens_q, max_q_len, spec_mask, stream);
 }

@@ -12,7 +12,9 @@
  *   - Pointers are DEVICE pointers unless the argument name starts with h_.
  *   - The caller owns every buffer (caches, page tables, outputs, workspace).
  *     The library allocates nothing, keeps no state between calls, never
- *     synchronises and never reads device memory from the host.
+ *     synchronises and never reads device memory from the host. The one
+ *     exception is pkv_batch_decode_with_kv_cache_no_alloc, which uses a
+ *     fixed device array of the library's own instead of a workspace.
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *     null stream). A call returns once the work is enqueued.
  *   - Validation uses host scalars and pointer non-nullness only. On any
@@ -42,7 +44,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 
 typedef enum {
   PKV_OK = 0,
@@ -242,6 +244,40 @@ pkv_status pkv_batch_decode_with_kv_cache(
     const void *query, const void *k_cache, const void *v_cache,
     int64_t page_stride_k, int64_t page_stride_v, void *workspace,
     size_t workspace_bytes, const int32_t *block_tables,
+    int32_t max_pages_per_seq, const uint32_t *seq_lens, int32_t batch_size,
+    int32_t max_seq_len, float bmm1_scale, float bmm2_scale,
+    int32_t window_left, void *out, pkv_dtype out_dtype, const float *sinks,
+    pkv_layout kv_layout, int32_t q_len_per_req, int32_t num_heads_qo,
+    int32_t num_heads_kv, int32_t head_dim, int32_t page_size,
+    pkv_dtype q_dtype, pkv_dtype kv_dtype, const float *bmm1_scale_dev,
+    const float *bmm2_scale_dev, float o_scale, const int32_t *cum_seq_lens_q,
+    int32_t max_q_len, const uint8_t *spec_mask, void *stream);
+
+/* Largest split-KV workspace pkv_batch_decode_with_kv_cache_no_alloc can
+ * serve from its static scratch array (bytes). */
+#define PKV_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* pkv_batch_decode_with_kv_cache without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. It calls no allocating
+ * routine. Arguments, results and errors are those of
+ * pkv_batch_decode_with_kv_cache; the split partials go to a file-scope
+ * device array of PKV_DECODE_SCRATCH_BYTES bytes inside the library instead
+ * of a caller's workspace (each GPU the library runs on holds its own copy
+ * until the process ends). Nothing in it needs clearing: the kernels read
+ * back only what the same call wrote.
+ *   - The array is shared by every call on one GPU: calls that overlap on
+ *     one GPU (on different streams, or from several threads) race on it
+ *     and give wrong results. Serialise them.
+ *   - The stream's device must be the current device (NULL stream: the
+ *     current device), since the array's address is per device.
+ *   - A call whose split plan needs more than PKV_DECODE_SCRATCH_BYTES
+ *     (pkv_decode_workspace_size(...) larger than that) returns
+ *     PKV_ERR_WORKSPACE_TOO_SMALL before any HIP call.
+ */
+pkv_status pkv_batch_decode_with_kv_cache_no_alloc(
+    const void *query, const void *k_cache, const void *v_cache,
+    int64_t page_stride_k, int64_t page_stride_v, const int32_t *block_tables,
     int32_t max_pages_per_seq, const uint32_t *seq_lens, int32_t batch_size,
     int32_t max_seq_len, float bmm1_scale, float bmm2_scale,
     int32_t window_left, void *out, pkv_dtype out_dtype, const float *sinks,

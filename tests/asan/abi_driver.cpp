@@ -124,6 +124,21 @@ int main() {
     a = p; a.layout = (pkv_layout)3; expect(a.call(), PKV_ERR_INVALID_ARG, "NHD or HND", "decode layout");
     a = p; a.max_pages = 1; expect(a.call(), PKV_ERR_INVALID_ARG, "too narrow", "decode narrow");
     a = p; a.batch = 0; if (a.call() != PKV_OK) { std::printf("FAIL decode empty\n"); ++failures; }
+    // the no-alloc variant: the same checks, plus the static scratch limit,
+    // all before any HIP call
+    auto no_alloc = [](const Decode &d) {
+      return pkv_batch_decode_with_kv_cache_no_alloc(
+          d.q, d.k, d.v, d.psk, d.psv, d.bt, d.max_pages, d.seq, d.batch, d.max_seq, d.bmm1,
+          d.bmm2, d.window, d.out, d.odt, d.sinks, d.layout, d.ql, d.hqo, d.hkv, d.d, d.ps,
+          d.qdt, d.kvdt, d.b1, d.b2, d.o_scale, d.cum, d.max_q, d.mask, nullptr);
+    };
+    a = p; a.window = -2;
+    expect(no_alloc(a), PKV_ERR_INVALID_ARG, "window_left", "no-alloc window");
+    a = p; a.d = 64; expect(no_alloc(a), PKV_ERR_UNSUPPORTED, "head_dim", "no-alloc d");
+    a = p; a.batch = 64; a.ql = 4; a.hqo = 64; a.max_seq = 1 << 20; a.max_pages = 1 << 16;
+    expect(no_alloc(a), PKV_ERR_WORKSPACE_TOO_SMALL, "static scratch", "no-alloc scratch");
+    a = p; a.batch = 0;
+    if (no_alloc(a) != PKV_OK) { std::printf("FAIL no-alloc empty\n"); ++failures; }
   }
   // ---- append and index math ------------------------------------------------------
   expect(pkv_append_paged_kv_cache(F, F, FI, FI, 10, const_cast<void *>(F), const_cast<void *>(F),

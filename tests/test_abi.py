@@ -29,14 +29,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
 
 
 def test_abi_version(lib):
-    assert lib.pkv_abi_version() == 3
+    assert lib.pkv_abi_version() == 4
 
 
 def _err(lib):
@@ -115,6 +115,45 @@ def test_decode_validation(lib, over, needle):
     st = _decode(lib, **over)
     assert st in (1, 2, 3)
     assert needle in _err(lib)
+
+
+def _decode_no_alloc(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, psk=2 * 16 * 8 * 128, psv=2 * 16 * 8 * 128, bt=FAKE,
+             max_pages=64, seq=FAKE, batch=4, max_seq=1024, bmm1=0.1, bmm2=1.0, window=-1,
+             out=FAKE, odt=1, sinks=None, layout=1, ql=1, hqo=32, hkv=8, d=128, ps=16, qdt=1,
+             kvdt=1, bmm1_dev=None, bmm2_dev=None, o_scale=1.0, cum_q=None, max_q=0, mask=None,
+             stream=None)
+    a.update(over)
+    return lib.pkv_batch_decode_with_kv_cache_no_alloc(*a.values())
+
+
+@pytest.mark.parametrize("over,needle", [
+    (dict(window=-2), "window_left"),
+    (dict(d=64), "head_dim"),
+    (dict(ql=3, hqo=32, hkv=1), "<= 64"),
+    (dict(kvdt=0), "kv dtype"),
+    (dict(max_pages=1), "too narrow"),
+    # a split plan larger than the static scratch array
+    (dict(batch=64, ql=4, hqo=64, hkv=8, max_seq=1 << 20, max_pages=1 << 16), "static scratch"),
+])
+def test_decode_no_alloc_validation(lib, over, needle):
+    # every check runs on host scalars before any HIP call, the scratch
+    # size check included
+    st = _decode_no_alloc(lib, **over)
+    assert st in (1, 2, 3)
+    msg = _err(lib)
+    assert needle in msg and "pkv_batch_decode_with_kv_cache_no_alloc" in msg
+
+
+def test_decode_no_alloc_scratch_limit(lib):
+    # the batch-decode workload's plan fits the static scratch array; a
+    # plan just over it is refused with PKV_ERR_WORKSPACE_TOO_SMALL
+    assert _lib.DECODE_SCRATCH_BYTES == 64 << 20
+    assert lib.pkv_decode_workspace_size(256, 1, 32, 8, 128, 8192, -1) <= _lib.DECODE_SCRATCH_BYTES
+    st = _decode_no_alloc(lib, batch=64, ql=4, hqo=64, hkv=8, max_seq=1 << 20, max_pages=1 << 16)
+    assert st == 3
+    assert lib.pkv_decode_workspace_size(64, 4, 64, 8, 128, 1 << 20, -1) > \
+        _lib.DECODE_SCRATCH_BYTES
 
 
 def test_append_validation(lib):
