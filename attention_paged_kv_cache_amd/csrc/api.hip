@@ -381,8 +381,11 @@ pkv_status decode_entry(
   CHECKF(num_heads_qo % num_heads_kv == 0, PKV_ERR_UNSUPPORTED,
          "num_heads_qo must be a multiple of num_heads_kv");
   CHECKF(head_dim == 128, PKV_ERR_UNSUPPORTED, "head_dim must be 128");
-  CHECKF((int64_t)q_max * (num_heads_qo / num_heads_kv) <= 64, PKV_ERR_UNSUPPORTED,
-         "q_len_per_req (or max_q_len) * num_heads_qo / num_heads_kv must be <= 64");
+  CHECKF((int64_t)q_max * (num_heads_qo / num_heads_kv) <= pkv::kDecodeMaxRows,
+         PKV_ERR_UNSUPPORTED,
+         "q_len_per_req (or max_q_len) * num_heads_qo / num_heads_kv must be <= 1024");
+  CHECKF(!spec_mask || q_max <= 64, PKV_ERR_UNSUPPORTED,
+         "with a spec_mask, q_len_per_req (or max_q_len) must be <= 64");
   CHECKF(kv_layout == PKV_NHD || kv_layout == PKV_HND, PKV_ERR_INVALID_ARG,
          "kv_layout must be NHD or HND");
   CHECKF(q_dtype == PKV_F16 || q_dtype == PKV_BF16, PKV_ERR_UNSUPPORTED,

@@ -1,6 +1,7 @@
 // Measured ceilings of the chip, against which the attention kernels' rates
 // are read beside the datasheet peaks: a bf16 matrix-core loop with no
-// memory traffic, and a streaming HBM read. Measurement only: nothing in the
+// memory traffic, a streaming HBM read and a streaming HBM copy (read plus
+// write, the traffic of an append). Measurement only: nothing in the
 // attention path calls these. Built into its own library.
 //
 // Each call validates its sizes on the host and launches one kernel on the
@@ -64,6 +65,31 @@ __global__ __launch_bounds__(256) void read_stream_kernel(const u32x4 *__restric
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
 }
 
+// Each workgroup copies its own contiguous span of per_wg16 16-byte vectors
+// from src to dst, kReadUnroll loads in flight per thread before their
+// stores; NT selects non-temporal (streaming) loads and stores.
+template <bool NT>
+__global__ __launch_bounds__(256) void copy_stream_kernel(const u32x4 *__restrict__ src,
+                                                          u32x4 *__restrict__ dst,
+                                                          int64_t per_wg16) {
+  const int64_t base = (int64_t)blockIdx.x * per_wg16 + threadIdx.x;
+  const u32x4 *q = src + base;
+  u32x4 *d = dst + base;
+  for (int64_t i = 0; i < per_wg16; i += 256 * kReadUnroll) {
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u)
+      v[u] = NT ? __builtin_nontemporal_load(q + i + 256 * u) : q[i + 256 * u];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) {
+      if (NT)
+        __builtin_nontemporal_store(v[u], d + i + 256 * u);
+      else
+        d[i + 256 * u] = v[u];
+    }
+  }
+}
+
 }  // namespace
 
 // `out` holds blocks * 256 floats. Returns a hipError_t value (0 = success).
@@ -90,5 +116,28 @@ CEIL_API int pkv_ceiling_read(const void *buf, int64_t bytes, int32_t blocks, ui
     return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(read_stream_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
                      (const u32x4 *)buf, bytes / 16 / blocks, out);
+  return (int)hipGetLastError();
+}
+
+// Copies `bytes` from `src` to `dst` (both 16-byte aligned, not
+// overlapping; bytes a multiple of blocks * 32 KiB, each workgroup taking an
+// equal contiguous span), with non-temporal loads and stores when
+// `nontemporal` is nonzero.
+CEIL_API int pkv_ceiling_copy(const void *src, void *dst, int64_t bytes, int32_t blocks,
+                              int32_t nontemporal, void *stream) {
+  const int64_t span = (int64_t)blocks * 256 * kReadUnroll * 16;
+  if (blocks <= 0 || bytes <= 0 || bytes % span || src == nullptr || dst == nullptr ||
+      (uintptr_t)src % 16 || (uintptr_t)dst % 16)
+    return (int)hipErrorInvalidValue;
+  const char *s = (const char *)src;
+  const char *d = (const char *)dst;
+  if (s < d + bytes && d < s + bytes) return (int)hipErrorInvalidValue;
+  if (nontemporal)
+    hipLaunchKernelGGL(copy_stream_kernel<true>, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const u32x4 *)src, (u32x4 *)dst, bytes / 16 / blocks);
+  else
+    hipLaunchKernelGGL(copy_stream_kernel<false>, dim3(blocks), dim3(256), 0,
+                       (hipStream_t)stream, (const u32x4 *)src, (u32x4 *)dst,
+                       bytes / 16 / blocks);
   return (int)hipGetLastError();
 }

@@ -39,7 +39,7 @@
 #include <algorithm>
 #include <type_traits>
 
-#include "launch.h"
+#include "launch_decode.h"
 #include "pkv_common.h"
 
 namespace pkv {
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
   if (a.mask) {  // uniform: every thread takes the barrier or none does
     if (tid < R) {
       uint64_t bits = 0;
-      if (tid < rows) {  // ql <= 64 because ql * G <= 64
+      if (tid < rows) {  // ql <= 64 whenever a mask is given
         const uint8_t *mrow = a.mask + ((int64_t)b * a.q_len + (row_base + tid) / G) * a.q_len;
         for (int i = 0; i < ql; ++i)
           if (mrow[i]) bits |= 1ull << i;

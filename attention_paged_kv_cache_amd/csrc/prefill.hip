@@ -52,7 +52,7 @@
 
 #include <type_traits>
 
-#include "launch.h"
+#include "launch_prefill.h"
 #include "pkv_common.h"
 
 namespace pkv {

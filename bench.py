@@ -14,11 +14,15 @@ on the host for comparison.
 
 Rates come from warm back-to-back calls; each leg also reports the median of
 calls made after a 1 GiB read has evicted the caches ("flushed"). The
-measured ceilings (a pure MFMA loop, a streaming read, a copy) put the rates
-beside what this GPU reaches at all.
+speculative step and the append page's Example (append then causal fp16
+prefill, launch-bound) are also timed as a captured HIP graph. The measured
+ceilings (a pure MFMA loop, a streaming read, copies) put the rates beside
+what this GPU reaches at all. The float64 oracle is timed on a bounded
+sample of every workload (cpu_baseline; its "configs" holds each one).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-       python bench.py --only {prefill,fp8prefill,decode,spec,append,copy,ceilings,append_sweep}
+       python bench.py --only {prefill,fp8prefill,decode,spec,append,copy,ceilings,append_sweep,
+                               example}
 """
 
 import argparse
@@ -57,7 +61,7 @@ def parse():
     p.add_argument("--no-flush", action="store_true",
                    help="skip the cold-cache timings and the measured ceilings (kernel traces)")
     p.add_argument("--only", choices=["prefill", "decode", "spec", "fp8prefill", "append", "copy",
-                                      "ceilings", "append_sweep"],
+                                      "ceilings", "append_sweep", "example"],
                    default=None, help="time one workload (profiling runs); 'copy' times a "
                                       "plain 1 GiB device copy used to calibrate HBM counters; "
                                       "'append_sweep' times the append at 2^12..2^20 rows of "
@@ -186,6 +190,13 @@ def time_flushed(fn, steps, flush):
     return _stats([a.elapsed_time(b) for a, b in ev], None)
 
 
+# Sources each kernel is compiled from: a counter summary taken on other
+# sources is not reported (an edit elsewhere leaves it valid).
+PREFILL_SRC = ("prefill.hip", "pkv_common.h", "launch_prefill.h")
+DECODE_SRC = ("decode.hip", "pkv_common.h", "launch_decode.h")
+APPEND_SRC = ("append.hip", "pkv_common.h", "launch_append.h")
+
+
 def kernel_hash(*files):
     h = hashlib.sha256()
     for f in files:
@@ -305,6 +316,66 @@ def bench_append(pkv, torch, w):
     return append_bytes(nnz, w["num_kv_heads"], w["head_dim"], elem), step
 
 
+def bench_example(pkv, torch, workloads):
+    """The append page's Example (fp16, NHD 5D cache, 4 requests of 45/8/25/22
+    tokens, 100 rows), then a causal prefill of the appended tokens. One step
+    is the whole chain: get_seq_lens, get_batch_indices_positions, append,
+    csr_to_block_tables, prefill. Returns (workload, prefill FLOP, append
+    bytes, step, append part, prefill part)."""
+    dev = "cuda:0"
+    w = workloads.append_example(dev)
+    cache = w["paged_kv_cache"]
+    indptr, last, idx, ai = (w[k].to(dev) for k in ("kv_indptr", "kv_last_page_len",
+                                                     "kv_indices", "append_indptr"))
+    lens = w["append_lengths"].to(dev)
+    ws = torch.zeros(pkv.prefill_workspace_size(4), dtype=torch.uint8, device=dev)
+    out = torch.empty(100, 32, 128, dtype=torch.float16, device=dev)
+    lse = torch.empty(100, 32, dtype=torch.float32, device=dev)
+
+    def append():
+        seq = pkv.get_seq_lens(indptr, last, 16)
+        bi, pos = pkv.get_batch_indices_positions(ai, seq, 100)
+        pkv.append_paged_kv_cache(w["k_append"], w["v_append"], bi, pos, cache, idx, indptr,
+                                  last, kv_layout="NHD")
+
+    def prefill():
+        bt = pkv.csr_to_block_tables(indptr, idx, 3)
+        pkv.batch_prefill_with_kv_cache(
+            w["q"], cache[:, 0], cache[:, 1], w["scale"], ws, max_token_per_sequence=45,
+            max_sequence_kv=45, actual_seq_lens_q=lens, actual_seq_lens_kv=lens,
+            block_tables=bt, causal=True, out=out, lse=lse, kv_layout="NHD")
+
+    def step():
+        append()
+        prefill()
+
+    L = w["append_lengths"].tolist()
+    flops = prefill_flops(L, L, 32, 128, 128)
+    # rows read and written, their indices, and the index arrays the chain reads
+    abytes = append_bytes(100, 32, 128, 2) + 4 * (5 + 4 + 8 + 5)
+    return w, flops, abytes, step, append, prefill
+
+
+def time_graph(torch, fn, steps, warmup):
+    """The same timing as time_steps for `fn` captured once in a HIP graph and
+    replayed: what the step costs on the GPU without the host's per-call
+    argument handling and launch gaps."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    t = time_steps(g.replay, steps, warmup)
+    del g
+    return t
+
+
 # ---- measured ceilings -------------------------------------------------------------
 
 def measured_ceilings(torch, steps=10):
@@ -352,17 +423,56 @@ def measured_ceilings(torch, steps=10):
     t = time_steps(lambda: y.copy_(x), steps, 3)
     copy = 2 * x.numel() * 4 / (t.median_ms * 1e-3) / 1e9
     del x, y
+
+    # hand-written streaming copy of 512 MiB (the bulk append's read and
+    # write sizes), plain and non-temporal loads and stores
+    lib.pkv_ceiling_copy.restype = ctypes.c_int
+    lib.pkv_ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    cbytes, cblocks = 512 << 20, 2048
+    src = torch.empty(cbytes, dtype=torch.uint8, device=dev).fill_(3)
+    dst = torch.empty_like(src)
+    kcopy = {}
+    for nt in (0, 1):
+        t = time_steps(lambda: ok(lib.pkv_ceiling_copy(src.data_ptr(), dst.data_ptr(), cbytes,
+                                                       cblocks, nt, stream), "copy stream"),
+                       steps, 3)
+        kcopy[nt] = 2 * cbytes / (t.median_ms * 1e-3) / 1e9
+    del src, dst
     torch.cuda.empty_cache()
     return {"mfma_bf16_loop_TFLOPs": round(mfma, 1), "hbm_read_4GiB_GBs": round(read, 1),
             "hbm_copy_1GiB_GBs": round(copy, 1),
+            "hbm_copy_kernel_512MiB_GBs": round(max(kcopy.values()), 1),
+            "hbm_copy_kernel_plain_GBs": round(kcopy[0], 1),
+            "hbm_copy_kernel_nontemporal_GBs": round(kcopy[1], 1),
             "what": "pure v_mfma_f32_32x32x16_bf16 loop (8 chains per wave, 8192 waves); "
                     "non-temporal 16-byte loads over 4 GiB (2048 workgroups, one contiguous "
-                    "span each); torch copy_ of 1 GiB (read + write counted); medians of 10 calls"}
+                    "span each); torch copy_ of 1 GiB (read + write counted); a hand-written "
+                    "copy of 512 MiB (2048 workgroups, one contiguous span each, 8 loads of 16 "
+                    "bytes in flight per thread before their stores; plain and non-temporal, "
+                    "the faster reported; read + write counted); medians of 10 calls"}
 
 
-def cpu_baseline(w, budget_s=12.0):
-    """The float64 oracle on a bounded sample of the prefill workload: whole
-    requests, in order, until about budget_s seconds of CPU work."""
+def _cpu_cores(torch):
+    cores = torch.get_num_threads()
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 0) for i in info] + [cores])
+    except Exception:
+        pass
+    return cores
+
+
+def _baseline(torch, value, unit, sample):
+    return {"value": value, "unit": unit, "cores": _cpu_cores(torch), "kind": "oracle",
+            "sample": f"{sample}; float64 numpy on {cpu_model()} "
+                      f"({os.cpu_count()} logical CPUs visible)"}
+
+
+def cpu_baseline(w, budget_s=6.0):
+    """The float64 oracle on a bounded sample of the batch-prefill workload:
+    whole requests, in order, until about budget_s seconds of CPU work."""
     import numpy as np
     import torch
     import oracle
@@ -374,34 +484,138 @@ def cpu_baseline(w, budget_s=12.0):
     cq = np.concatenate([[0], np.cumsum(lq.numpy())])
     flops = 0
     n_req = 0
-    t0 = time.perf_counter()
+    spent = 0.0
     for b in range(lq.shape[0]):
         n = (int(lkv[b]) + ps - 1) // ps
         bt = w["block_tables"][b:b + 1]
         kc, bt1 = compact_pages(w["k_cache"], bt, [n])
         vc, _ = compact_pages(w["v_cache"], bt, [n])
+        kb, vb = bits(kc), bits(vc)
         q = q_all[cq[b]:cq[b + 1]]
-        oracle.batch_prefill(q, fmt(w["q"]), bits(kc), bits(vc), fmt(w["k_cache"]), bt1.numpy(),
+        t0 = time.perf_counter()
+        oracle.batch_prefill(q, fmt(w["q"]), kb, vb, fmt(w["k_cache"]), bt1.numpy(),
                              lq[b:b + 1].numpy(), lkv[b:b + 1].numpy(), w["scale"], True,
                              w["layout"])
+        spent += time.perf_counter() - t0
         flops += prefill_flops([int(lq[b])], [int(lkv[b])], w["num_qo_heads"], w["d_qk"],
                                w["d_vo"])
         n_req += 1
-        if time.perf_counter() - t0 > budget_s:
+        if spent > budget_s:
             break
+    return _baseline(torch, round(flops / spent / 1e12, 6), "TFLOP/s",
+                     f"first {n_req} of {lq.shape[0]} requests of the batch-prefill workload "
+                     f"({flops / 1e9:.1f} GFLOP algorithmic) in {spent:.1f} s")
+
+
+def cpu_example(w, reps=3):
+    """The oracle on the whole append Example plus its causal prefill (the
+    same chain as the GPU step: seq lens, row coordinates, append, block
+    tables, prefill), the fastest of `reps` runs. Only the 8 pages the
+    Example uses are handed over (the append touches nothing else)."""
+    import numpy as np
+    import torch
+    import oracle
+    from tests.helpers import bits, fmt
+    cache = bits(w["paged_kv_cache"][:8])
+    kb, vb, qb = bits(w["k_append"]), bits(w["v_append"]), bits(w["q"])
+    indptr, last = w["kv_indptr"].numpy(), w["kv_last_page_len"].numpy()
+    idx, ai = w["kv_indices"].numpy(), w["append_indptr"].numpy()
+    L = w["append_lengths"].numpy()
+    f = fmt(w["q"])
+    best = float("inf")
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        seq = oracle.get_seq_lens(indptr, last, 16)
+        bi, pos = oracle.get_batch_indices_positions(ai, seq, 100)
+        kc, vc = cache[:, 0].copy(), cache[:, 1].copy()
+        oracle.append_paged_kv_cache(kb, vb, bi, pos, kc, vc, idx, indptr, last, "NHD")
+        bt = oracle.csr_to_block_tables(indptr, idx, 3)
+        oracle.batch_prefill(qb, f, kc, vc, f, bt, L, L, w["scale"], True, "NHD")
+        best = min(best, time.perf_counter() - t0)
+    flops = prefill_flops(L.tolist(), L.tolist(), 32, 128, 128)
+    return _baseline(torch, round(best * 1e6, 1), "us per step",
+                     f"the whole append Example (100 rows) and its causal prefill "
+                     f"({flops / 1e6:.1f} MFLOP, {flops / best / 1e9:.3f} GFLOP/s), fastest of "
+                     f"{reps} runs")
+
+
+def cpu_fp8_prefill(w, n_req=2, rows_per_req=12, seed=0):
+    """The oracle on sampled query rows of the fp8 prefill workload (all
+    heads of each row; the request's pages are gathered and decoded as part
+    of the timed call)."""
+    import numpy as np
+    import torch
+    import oracle
+    from tests.helpers import bits, fmt
+    from workloads import compact_pages
+    rng = np.random.default_rng(seed)
+    lq = w["seq_lens_q"].numpy()
+    rows = [(b, int(t)) for b in range(n_req) for t in rng.integers(0, lq[b], rows_per_req)]
+    ps = w["page_size"]
+    used = [(int(w["seq_lens_kv"][b]) + ps - 1) // ps if b < n_req else 0
+            for b in range(len(lq))]
+    kc, bt = compact_pages(w["k_cache"], w["block_tables"], used)
+    vc, _ = compact_pages(w["v_cache"], w["block_tables"], used)
+    kb, vb, qb = bits(kc), bits(vc), bits(w["q"])
+    sc = lambda x: float(x.reshape(-1)[0])
+    t0 = time.perf_counter()
+    oracle.batch_prefill(qb, fmt(w["q"]), kb, vb, fmt(w["k_cache"]), bt.numpy(), lq,
+                         w["seq_lens_kv"].numpy(), w["scale"], True, w["layout"],
+                         q_scale=sc(w["q_scale"]), k_scale=sc(w["k_scale"]),
+                         v_scale=sc(w["v_scale"]), rows=rows)
     dt = time.perf_counter() - t0
-    cores = torch.get_num_threads()
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max([i.get("num_threads", 0) for i in info] + [cores])
-    except Exception:
-        pass
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"first {n_req} of 16 requests of the prefill workload "
-                      f"({flops / 1e9:.1f} GFLOP algorithmic) in {dt:.1f} s, float64 numpy "
-                      f"on {cpu_model()} ({os.cpu_count()} logical CPUs visible)"}
+    shift = int(w["seq_lens_kv"][0]) - int(lq[0])
+    pairs = sum(t + 1 + shift for _, t in rows)
+    flops = 2 * (w["d_qk"] + w["d_vo"]) * w["num_qo_heads"] * pairs
+    return _baseline(torch, round(flops / dt / 1e12, 6), "TFLOP/s",
+                     f"{len(rows)} random query rows (all {w['num_qo_heads']} heads) of the first {n_req} "
+                     f"requests of the fp8 prefill workload ({flops / 1e9:.2f} GFLOP "
+                     f"algorithmic) in {dt:.1f} s")
+
+
+def cpu_decode(w, reqs, append=False):
+    """The oracle on a sample of whole requests of a decode workload (with
+    `append`: the speculative step, the 4 draft rows of each sampled request
+    appended by the oracle first). Returns (time, decode bytes of the
+    sample)."""
+    import numpy as np
+    import torch
+    import oracle
+    from tests.helpers import bits, fmt
+    from workloads import compact_pages
+    ps = w["page_size"]
+    seq = w["seq_lens"].to(torch.int64)
+    used = [0] * seq.shape[0]
+    for b in reqs:
+        used[b] = (int(seq[b]) + ps - 1) // ps
+    sub, bt = compact_pages(w["kv_cache"], w["block_tables"], used)
+    kb, vb = bits(sub[:, 0]), bits(sub[:, 1])
+    qb = bits(w["query"])
+    sinks = None if w["sinks"] is None else w["sinks"].double().numpy()
+    ql = w["q_len_per_req"]
+    if append:
+        ka, va = bits(w["k_append"]), bits(w["v_append"])
+        # the sampled requests' CSR page lists, renumbered into the compacted pool
+        n_pages = [used[b] for b in reqs]
+        indptr = np.concatenate([[0], np.cumsum(n_pages)]).astype(np.int32)
+        idx = np.concatenate([bt[b, :used[b]].numpy() for b in reqs]).astype(np.int32)
+        last = np.array([(int(seq[b]) - 1) % ps + 1 for b in reqs], dtype=np.int32)
+        ai = np.arange(len(reqs) + 1, dtype=np.int32) * ql
+        rows = np.concatenate([np.arange(b * ql, (b + 1) * ql) for b in reqs])
+        ka_s, va_s = ka[rows], va[rows]
+    t0 = time.perf_counter()
+    if append:
+        s_seq = oracle.get_seq_lens(indptr, last, ps)
+        bi, pos = oracle.get_batch_indices_positions(ai, s_seq, len(rows))
+        oracle.append_paged_kv_cache(ka_s, va_s, bi, pos, kb, vb, idx, indptr, last, w["layout"])
+    oracle.batch_decode(qb, fmt(w["query"]), kb, vb, fmt(w["kv_cache"]), bt.numpy(),
+                        seq.numpy(), w["bmm1_scale"], w["bmm2_scale"], w["window_left"], sinks,
+                        w["layout"], ql, requests=reqs)
+    dt = time.perf_counter() - t0
+    elem = w["kv_cache"].element_size()
+    nbytes = decode_bytes([int(seq[b]) for b in reqs], ql, w["window_left"],
+                          w["num_qo_heads"], w["num_kv_heads"], w["head_dim"], elem, 2, 2, ps)
+    return dt, nbytes
 
 
 def cpu_model():
@@ -417,6 +631,14 @@ def cpu_model():
 
 def rate(work, ms, scale):
     return work / (ms * 1e-3) / scale
+
+
+def mixed_fp8_peak(d_qk, d_vo):
+    """Dense peak of a prefill whose QK^T runs on fp8 MFMA and whose PV runs
+    on bf16 MFMA (P is rounded to bf16): each part at its own peak, in
+    proportion to its share of the FLOP."""
+    share_qk = d_qk / (d_qk + d_vo)
+    return 1.0 / (share_qk / PEAK_FP8_TFLOPS + (1.0 - share_qk) / PEAK_BF16_TFLOPS)
 
 
 def main():
@@ -435,17 +657,19 @@ def main():
         only(args, torch, pkv, workloads)
         return
 
-    prefill_src = ("prefill.hip", "pkv_common.h", "launch.h")
-    decode_src = ("decode.hip", "pkv_common.h", "launch.h")
-    append_src = ("append.hip", "pkv_common.h", "launch.h")
     flush = None if args.no_flush else new_flush_buffer(torch)
     T, G = 1e12, 1e9
+    cpu = not args.no_cpu_baseline
+    base = {}
 
     print("bench: prefill (bf16, batch 16)", file=sys.stderr, flush=True)
     w, flops, step = bench_prefill(pkv, torch, workloads)
     t1 = time_steps(step, args.steps, args.warmup)
     f1 = time_flushed(step, args.steps, flush)
     tokens, kv_tokens = int(w["seq_lens_q"].sum()), int(w["seq_lens_kv"].sum())
+    if cpu:
+        print("bench: float64 oracle, batch prefill sample", file=sys.stderr, flush=True)
+        base["batch_prefill"] = cpu_baseline(w)
     del w, step
     torch.cuda.empty_cache()
 
@@ -453,6 +677,9 @@ def main():
     w, flops3, step = bench_prefill(pkv, torch, workloads, fp8=True)
     t3 = time_steps(step, args.steps, args.warmup)
     f3 = time_flushed(step, args.steps, flush)
+    if cpu:
+        print("bench: float64 oracle, fp8 prefill sample", file=sys.stderr, flush=True)
+        base["fp8_prefill"] = cpu_fp8_prefill(w)
     del w, step
     torch.cuda.empty_cache()
 
@@ -460,6 +687,13 @@ def main():
     w, bytes4, step = bench_decode(pkv, torch, workloads)
     t4 = time_steps(step, args.steps, args.warmup)
     f4 = time_flushed(step, args.steps, flush)
+    if cpu:
+        print("bench: float64 oracle, decode sample", file=sys.stderr, flush=True)
+        reqs = list(range(24))
+        dt, nb = cpu_decode(w, reqs)
+        base["decode"] = _baseline(torch, round(nb / dt / 1e9, 4), "GB/s",
+                                   f"the first {len(reqs)} of 256 requests of the decode "
+                                   f"workload ({nb / 1e6:.1f} MB algorithmic) in {dt:.1f} s")
     del w, step
     torch.cuda.empty_cache()
 
@@ -474,6 +708,16 @@ def main():
     t5d = time_steps(decode5, args.steps, args.warmup)
     t5a = time_steps(append5, args.steps, args.warmup)
     f5d = time_flushed(decode5, args.steps, flush)
+    t5g = time_graph(torch, step5, args.steps, args.warmup)
+    t5ag = time_graph(torch, append5, args.steps, args.warmup)
+    if cpu:
+        print("bench: float64 oracle, speculative step sample", file=sys.stderr, flush=True)
+        reqs = [0, 1, 2, 3]
+        dt, nb = cpu_decode(w, reqs, append=True)
+        base["spec_decode"] = _baseline(
+            torch, round(nb / dt / 1e9, 4), "GB/s",
+            f"requests 0-3 of 64 of the speculative step, their 16 draft rows appended "
+            f"and their 16 queries decoded ({nb / 1e6:.1f} MB of decode reads) in {dt:.1f} s")
     del w, append5, decode5
     torch.cuda.empty_cache()
 
@@ -483,12 +727,24 @@ def main():
     t6 = time_steps(step, args.steps, args.warmup)
     f6 = time_flushed(step, args.steps, flush)
     del w, step
+    torch.cuda.empty_cache()
+
+    print("bench: append example + causal prefill (fp16, NHD)", file=sys.stderr, flush=True)
+    w, flops0, abytes0, step0, append0, prefill0 = bench_example(pkv, torch, workloads)
+    t0s = time_steps(step0, args.steps, args.warmup)
+    t0a = time_steps(append0, args.steps, args.warmup)
+    t0p = time_steps(prefill0, args.steps, args.warmup)
+    t0g = time_graph(torch, step0, args.steps, args.warmup)
+    if cpu:
+        print("bench: float64 oracle, append example", file=sys.stderr, flush=True)
+        base["append_example"] = cpu_example(w)
+    del w, step0, append0, prefill0
     flush = None
     torch.cuda.empty_cache()
 
     ceil = None
     if not args.no_flush:
-        print("bench: measured ceilings (MFMA loop, HBM read, copy)", file=sys.stderr,
+        print("bench: measured ceilings (MFMA loop, HBM read, copies)", file=sys.stderr,
               flush=True)
         ceil = measured_ceilings(torch)
 
@@ -504,6 +760,7 @@ def main():
     d4_l = rate(bytes4, t4.launch_ms, G)
     d5_l = rate(bytes5, t5d.launch_ms, G)
     a6_l = rate(bytes6, t6.launch_ms, G)
+    mixed = mixed_fp8_peak(192, 128)
     line = {
         "metric": METRIC,
         "value": round(rate(flops, t1.region_ms, T), 2),
@@ -528,7 +785,7 @@ def main():
             "flop_per_step": flops,
         },
         "roofline": roofline("mfma", p_l, PEAK_BF16_TFLOPS, "TFLOP/s",
-                             traffic("prefill_bf16", prefill_src)),
+                             traffic("prefill_bf16", PREFILL_SRC)),
         "timing": timing(t1, f1, flops, T),
         "fp8_prefill": {
             "workload": "e4m3 prefill, d_qk 192 / d_vo 128, batch 8, q_len = kv_len = 4096, "
@@ -536,8 +793,10 @@ def main():
             "value": round(rate(flops3, t3.region_ms, T), 2), "unit": "TFLOP/s",
             "ms_per_step": round(t3.region_ms, 4),
             "roofline": roofline("mfma", p3_l, PEAK_FP8_TFLOPS, "TFLOP/s",
-                                 traffic("prefill_e4m3_d192", prefill_src)),
+                                 traffic("prefill_e4m3_d192", PREFILL_SRC)),
             "frac_of_bf16_peak": round(p3_l / PEAK_BF16_TFLOPS, 4),
+            "mixed_peak_TFLOPs": round(mixed, 1),
+            "frac_of_mixed_peak": round(p3_l / mixed, 4),
             **timing(t3, f3, flops3, T),
         },
         "decode": {
@@ -546,7 +805,7 @@ def main():
             "value": round(rate(bytes4, t4.region_ms, G), 1), "unit": "GB/s",
             "ms_per_step": round(t4.region_ms, 4), "bytes_per_step": bytes4,
             "roofline": roofline("hbm", d4_l, PEAK_HBM_GBS, "GB/s",
-                                 traffic("decode_bf16", decode_src)),
+                                 traffic("decode_bf16", DECODE_SRC)),
             **timing(t4, f4, bytes4, G),
         },
         "spec_decode": {
@@ -554,13 +813,17 @@ def main():
                         "seq U[4096,32768], 64/8 heads, d 128, HND page 32, window_left 4095, "
                         "sinks, q_len_per_req 4",
             "ms_per_step": round(t5.region_ms, 4),
+            "graph_ms_per_step": round(t5g.region_ms, 4),
             "decode_value": round(d5_l, 1), "unit": "GB/s",
             "decode_bytes": bytes5,
             "roofline": roofline("hbm", d5_l, PEAK_HBM_GBS, "GB/s",
-                                 traffic("spec_decode_e4m3", decode_src)),
+                                 traffic("spec_decode_e4m3", DECODE_SRC)),
             "decode": timing(t5d, f5d, bytes5, G),
             "append_ms": round(t5a.launch_ms, 4),
+            "append_graph_ms": round(t5ag.launch_ms, 4),
             "append_GBs": round(rate(abytes5, t5a.launch_ms, G), 1),
+            "append_roofline": roofline("hbm", rate(abytes5, t5ag.launch_ms, G), PEAK_HBM_GBS,
+                                        "GB/s", traffic("append_spec_e4m3", APPEND_SRC)),
         },
         "bulk_append": {
             "workload": "append 1024 rows into each of 256 requests: e4m3 KV, 8 kv heads, d 128, "
@@ -568,8 +831,23 @@ def main():
             "value": round(rate(bytes6, t6.region_ms, G), 1), "unit": "GB/s",
             "ms_per_step": round(t6.region_ms, 4), "bytes_per_step": bytes6,
             "roofline": roofline("hbm", a6_l, PEAK_HBM_GBS, "GB/s",
-                                 traffic("append_bulk_e4m3", append_src)),
+                                 traffic("append_bulk_e4m3", APPEND_SRC)),
             **timing(t6, f6, bytes6, G),
+        },
+        "append_example": {
+            "workload": "the append page's Example (fp16, NHD 5D cache of 1000 pages x 16 "
+                        "tokens x 32 heads x 128, 100 rows into 4 requests of 45/8/25/22 "
+                        "tokens) then a causal fp16 prefill of those tokens (32/32 heads, "
+                        "scale 1/sqrt(128), fp32 LSE): get_seq_lens, "
+                        "get_batch_indices_positions, append, csr_to_block_tables, prefill",
+            "us_per_step": round(t0s.region_ms * 1e3, 2),
+            "graph_us_per_step": round(t0g.region_ms * 1e3, 2),
+            "us_median": round(t0s.median_ms * 1e3, 2), "us_min": round(t0s.min_ms * 1e3, 2),
+            "append_us": round(t0a.launch_ms * 1e3, 2),
+            "prefill_us": round(t0p.launch_ms * 1e3, 2),
+            "append_GBs": round(rate(abytes0, t0a.launch_ms, G), 1),
+            "prefill_TFLOPs": round(rate(flops0, t0p.launch_ms, T), 3),
+            "bound": "launch latency (3.3 MB moved, 27 MFLOP)",
         },
     }
     if ceil is not None:
@@ -579,11 +857,13 @@ def main():
             "decode_frac_of_read": round(d4_l / ceil["hbm_read_4GiB_GBs"], 4),
             "spec_decode_frac_of_read": round(d5_l / ceil["hbm_read_4GiB_GBs"], 4),
             "bulk_append_frac_of_copy": round(a6_l / ceil["hbm_copy_1GiB_GBs"], 4),
+            "bulk_append_frac_of_copy_kernel": round(
+                a6_l / ceil["hbm_copy_kernel_512MiB_GBs"], 4),
         }
-    if not args.no_cpu_baseline:
-        print("bench: float64 oracle on the host (bounded sample)", file=sys.stderr, flush=True)
-        w, _, _ = bench_prefill(pkv, torch, workloads)
-        line["cpu_baseline"] = cpu_baseline(w)
+    if cpu:
+        head = dict(base["batch_prefill"])
+        head["configs"] = base
+        line["cpu_baseline"] = head
     print(json.dumps(line), flush=True)
 
 
@@ -618,6 +898,10 @@ def only(args, torch, pkv, workloads):
              "ms_append": ta.launch_ms}
     elif args.only == "ceilings":
         r = measured_ceilings(torch)
+    elif args.only == "example":
+        w, flops0, abytes0, step0, _, _ = bench_example(pkv, torch, workloads)
+        t = time_steps(step0, args.steps, args.warmup)
+        r = {"us_per_step": t.region_ms * 1e3, "us_median": t.median_ms * 1e3}
     else:  # append_sweep
         flush = new_flush_buffer(torch)
         for k in range(12, 21):

@@ -238,7 +238,8 @@ size_t pkv_decode_workspace_size(int32_t batch_size, int32_t q_len_per_req,
  *         and window_left still applies (to positions).
  *   workspace >= pkv_decode_workspace_size(...) bytes (contents ignored)
  * Supported: head_dim == 128, num_heads_qo % num_heads_kv == 0,
- * Q * num_heads_qo / num_heads_kv <= 64, page_size in {16, 32, 64}.
+ * Q * num_heads_qo / num_heads_kv <= 1024 (query rows per kv head), Q <= 64
+ * when spec_mask is given, page_size in {16, 32, 64}.
  */
 pkv_status pkv_batch_decode_with_kv_cache(
     const void *query, const void *k_cache, const void *v_cache,

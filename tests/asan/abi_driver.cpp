@@ -111,7 +111,9 @@ int main() {
     Decode a = p; a.window = -2; expect(a.call(), PKV_ERR_INVALID_ARG, "window_left", "decode window");
     a = p; a.ql = 0; expect(a.call(), PKV_ERR_INVALID_ARG, "q_len_per_req", "decode ql");
     a = p; a.d = 64; expect(a.call(), PKV_ERR_UNSUPPORTED, "head_dim", "decode d");
-    a = p; a.ql = 3; a.hkv = 1; expect(a.call(), PKV_ERR_UNSUPPORTED, "<= 64", "decode rows");
+    a = p; a.ql = 33; a.hkv = 1; expect(a.call(), PKV_ERR_UNSUPPORTED, "<= 1024", "decode rows");
+    a = p; a.ql = 65; a.hqo = 8; a.mask = reinterpret_cast<const uint8_t *>(F);
+    expect(a.call(), PKV_ERR_UNSUPPORTED, "spec_mask", "decode mask drafts");
     a = p; a.qdt = PKV_E4M3; expect(a.call(), PKV_ERR_UNSUPPORTED, "query dtype", "decode qdt");
     a = p; a.kvdt = PKV_F16; expect(a.call(), PKV_ERR_UNSUPPORTED, "kv dtype", "decode kvdt");
     a = p; a.odt = PKV_E4M3; a.o_scale = 0.0f; expect(a.call(), PKV_ERR_INVALID_ARG, "o_scale", "decode o_scale");

@@ -95,7 +95,8 @@ def _decode(lib, **over):
     (dict(window=-2), "window_left"),
     (dict(ql=0), "q_len_per_req"),
     (dict(d=64), "head_dim"),
-    (dict(ql=3, hqo=32, hkv=1), "<= 64"),
+    (dict(ql=33, hqo=32, hkv=1), "<= 1024"),
+    (dict(ql=65, hqo=8, hkv=8, mask=FAKE), "spec_mask"),
     (dict(qdt=2), "query dtype"),
     (dict(kvdt=0), "kv dtype"),
     (dict(ws_bytes=0, max_seq=100000, max_pages=10000), "workspace"),
@@ -109,7 +110,7 @@ def _decode(lib, **over):
     (dict(odt=7), "output dtype"),
     (dict(cum_q=FAKE, max_q=0), "max_q_len"),
     (dict(cum_q=None, max_q=3), "max_q_len"),
-    (dict(cum_q=FAKE, max_q=17, hqo=32, hkv=8), "<= 64"),
+    (dict(cum_q=FAKE, max_q=257, hqo=32, hkv=8), "<= 1024"),
 ])
 def test_decode_validation(lib, over, needle):
     st = _decode(lib, **over)
@@ -130,7 +131,7 @@ def _decode_no_alloc(lib, **over):
 @pytest.mark.parametrize("over,needle", [
     (dict(window=-2), "window_left"),
     (dict(d=64), "head_dim"),
-    (dict(ql=3, hqo=32, hkv=1), "<= 64"),
+    (dict(ql=33, hqo=32, hkv=1), "<= 1024"),
     (dict(kvdt=0), "kv dtype"),
     (dict(max_pages=1), "too narrow"),
     # a split plan larger than the static scratch array

@@ -546,3 +546,25 @@ def test_full_size_spec_decode_mask_and_offsets_reproduce_causal(pkv):
     cum = (np.arange(65) * 4).astype(np.int32)
     c = run_ragged(pkv, w, cum, 4)
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+@pytest.mark.parametrize("ql,hqo,hkv,seq,window,masked,seed", [
+    (16, 64, 8, (1, 900), -1, False, 160),        # 128 rows: 16 drafts x GQA 8, one split
+    (16, 64, 8, (20000, 40000), -1, True, 161),   # 128 rows, split partials, tree mask
+    (32, 64, 8, (100, 3000), 500, False, 162),    # 256 rows
+    (64, 16, 1, (50, 700), -1, True, 163),        # 1024 rows: 64 drafts x GQA 16, mask
+])
+def test_more_than_64_rows(pkv, ql, hqo, hkv, seq, window, masked, seed):
+    # more query rows per kv head than one 64-bit mask word: groups of 32
+    # rows, one workgroup each, on one XCD; the draft mask stays one word
+    # per row (at most 64 drafts)
+    w = small(seed=seed, seq=seq, batch=3, q_len_per_req=ql, num_qo_heads=hqo,
+              num_kv_heads=hkv, window_left=window, sinks=True,
+              kv_dtype=torch.float8_e4m3fn if seed % 2 else torch.bfloat16, page_size=32)
+    cum = (np.arange(4) * ql).astype(np.int32)
+    mask = None
+    if masked:
+        mask = torch.from_numpy(_tree_mask(3, ql, np.random.default_rng(seed))).to(DEV)
+    got = run_ragged(pkv, w, None, ql, mask=mask)
+    err = assert_out_close(got, oracle_decode_ragged(w, cum, mask), got.dtype)
+    print(f"{ql * hqo // hkv} rows: max |out err| {err:.3g}", flush=True)

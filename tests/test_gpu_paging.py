@@ -88,6 +88,32 @@ def test_append_example_bit_exact(pkv):
     assert not np.array_equal(got, before)
 
 
+def test_streaming_append_bitwise(pkv):
+    # an append whose rows reach the 256 MiB from which the kernel uses
+    # non-temporal loads and stores (131072 e4m3 rows of 8 heads x 128 for
+    # K and V, into 64 requests' random pages): the whole cache, touched and
+    # untouched bytes, equals the oracle's bit for bit
+    w = workloads.bulk_append(DEV, seed=61, batch=64, seq=(4096, 8192), rows=2048)
+    nnz = w["k_append"].shape[0]
+    assert 2 * w["k_append"].numel() * w["k_append"].element_size() >= 256 << 20
+    kv = w["kv_cache"]
+    before = bits(kv)
+    bi, pos = pkv.get_batch_indices_positions(w["append_indptr"].to(DEV),
+                                              w["seq_lens"].to(DEV), nnz)
+    pkv.append_paged_kv_cache(w["k_append"], w["v_append"], bi, pos, kv,
+                              w["kv_indices"].to(DEV), w["kv_indptr"].to(DEV),
+                              w["kv_last_page_len"].to(DEV), kv_layout="HND")
+    torch.cuda.synchronize()
+    ref = before.copy()
+    oracle.append_paged_kv_cache(bits(w["k_append"]), bits(w["v_append"]), bi.cpu().numpy(),
+                                 pos.cpu().numpy(), ref[:, 0], ref[:, 1],
+                                 w["kv_indices"].numpy(), w["kv_indptr"].numpy(),
+                                 w["kv_last_page_len"].numpy(), "HND")
+    got = bits(kv)
+    assert np.array_equal(got, ref)
+    assert not np.array_equal(got, before)
+
+
 @pytest.mark.parametrize("layout,dtype,ps,tuple_form,B,H,D,seq_lo,seq_hi,app_hi", [
     ("HND", torch.bfloat16, 16, False, 5, 3, 128, 1, 200, 40),
     ("NHD", torch.float16, 32, True, 5, 3, 128, 1, 200, 40),
