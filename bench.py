@@ -539,7 +539,7 @@ def cpu_example(w, reps=3):
                      f"{reps} runs")
 
 
-def cpu_fp8_prefill(w, n_req=2, rows_per_req=12, seed=0):
+def cpu_fp8_prefill(w, n_req=4, rows_per_req=64, seed=0):
     """The oracle on sampled query rows of the fp8 prefill workload (all
     heads of each row; the request's pages are gathered and decoded as part
     of the timed call)."""
@@ -689,7 +689,7 @@ def main():
     f4 = time_flushed(step, args.steps, flush)
     if cpu:
         print("bench: float64 oracle, decode sample", file=sys.stderr, flush=True)
-        reqs = list(range(24))
+        reqs = list(range(96))
         dt, nb = cpu_decode(w, reqs)
         base["decode"] = _baseline(torch, round(nb / dt / 1e9, 4), "GB/s",
                                    f"the first {len(reqs)} of 256 requests of the decode "
@@ -712,12 +712,13 @@ def main():
     t5ag = time_graph(torch, append5, args.steps, args.warmup)
     if cpu:
         print("bench: float64 oracle, speculative step sample", file=sys.stderr, flush=True)
-        reqs = [0, 1, 2, 3]
+        reqs = list(range(16))
         dt, nb = cpu_decode(w, reqs, append=True)
         base["spec_decode"] = _baseline(
             torch, round(nb / dt / 1e9, 4), "GB/s",
-            f"requests 0-3 of 64 of the speculative step, their 16 draft rows appended "
-            f"and their 16 queries decoded ({nb / 1e6:.1f} MB of decode reads) in {dt:.1f} s")
+            f"requests 0-{len(reqs) - 1} of 64 of the speculative step, their "
+            f"{4 * len(reqs)} draft rows appended and their {4 * len(reqs)} queries decoded "
+            f"({nb / 1e6:.1f} MB of decode reads) in {dt:.1f} s")
     del w, append5, decode5
     torch.cuda.empty_cache()
 
