@@ -273,6 +273,7 @@ PKV_API pkv_status pkv_batch_prefill_with_kv_cache(
   a.d_vo = d_vo;
   a.page_size = paged ? page_size : 16;  // unpaged: 16-row groups per wave
   a.max_q = max_token_per_sequence;
+  a.max_kv = max_sequence_kv;
   a.causal = causal ? 1 : 0;
   a.scale = scale;
   a.q_scale = q_scale;

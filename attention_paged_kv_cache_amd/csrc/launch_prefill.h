@@ -32,6 +32,7 @@ struct PrefillArgs {
   int32_t max_pages;
   int32_t batch, num_heads_qo, num_heads_kv, d_qk, d_vo, page_size;
   int32_t max_q;
+  int32_t max_kv;  // >= every L_kv (sizes the tile dispatch batches)
   int32_t causal;
   float scale;
   const float *q_scale, *k_scale, *v_scale;

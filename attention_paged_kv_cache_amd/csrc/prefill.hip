@@ -50,6 +50,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "launch_prefill.h"
@@ -169,7 +170,7 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 template <class ET, int DQK, class OT, bool PAGED>
 __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void prefill_kernel(
     PrefillArgs a, int32_t T, int32_t Gc, int32_t head_chunks,
-    int32_t n_qtiles) {
+    int32_t n_qtiles, int32_t S) {
   using G_ = Geo<ET, DQK>;
   using PT = typename PvTag<ET>::type;
   constexpr int ES = G_::ES;
@@ -190,14 +191,21 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   // Workgroups are dispatched round-robin over the 8 XCDs (block i runs on
   // XCD i % 8), each with its own L2. A "pair" (request, kv head, head
   // chunk) owns one K/V stream; all query tiles of a pair are mapped to the
-  // same XCD and dispatched back to back, heaviest (last) tile first, so
-  // the pair's K/V pages are fetched from HBM once and re-read from L2.
+  // same XCD, so the pair's K/V pages are fetched from HBM about once and
+  // re-read from L2. An XCD's pairs are taken S at a time (a batch sized
+  // so that its K/V streams fit the XCD's L2); within a batch the tiles go
+  // by query-tile index from the last (the heaviest under the causal mask)
+  // down, cycling over the batch's pairs. Dispatching heavy tiles first
+  // keeps the grid's tail made of light tiles.
   const int n_pairs = a.batch * a.num_heads_kv * head_chunks;
   const int xcd = blockIdx.x % kXcds;
   const int slot_in_xcd = blockIdx.x / kXcds;
-  const int pair = xcd + kXcds * (slot_in_xcd / n_qtiles);
+  const int per_batch = S * n_qtiles;
+  const int batch_i = slot_in_xcd / per_batch;
+  const int r_in = slot_in_xcd - batch_i * per_batch;
+  const int pair = xcd + kXcds * (batch_i * S + r_in % S);
   if (pair >= n_pairs) return;
-  const int qtile = n_qtiles - 1 - slot_in_xcd % n_qtiles;
+  const int qtile = n_qtiles - 1 - r_in / S;
   const int b = pair / (a.num_heads_kv * head_chunks);
   const int kvh = (pair / head_chunks) % a.num_heads_kv;
   const int hc = pair % head_chunks;
@@ -557,6 +565,18 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
         l_tot > 0.0f ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
 }
 
+// Pairs per dispatch batch of one XCD: the largest power of two (at most 8)
+// of K/V streams of the longest request that fits three quarters of the
+// XCD's 4 MB L2 (the rest holds the tiles' Q, output and DMA traffic).
+// Measured on one MI355X (TFLOP/s by pairs per batch 1 / 2 / 4 / 8):
+// batch prefill bf16, 2 MB streams: 966 / 839 / 751 / 761 (a second
+// stream overflows the L2); fp8 prefill d_qk 192, 1.3 MB streams of 4096
+// tokens: 1300 / 1349 / 1392 / 1384 (interleaving identical long causal
+// streams ends the grid on light tiles). 3 pairs per batch measured 1294 on
+// the fp8 workload (16 pairs per XCD leave a lone last pair, whose heavy
+// tiles then end the grid), hence powers of two.
+constexpr int64_t kStreamBytesPerXcd = (int64_t)3 << 20;
+
 template <class ET, int DQK, class OT>
 hipError_t launch_typed(const PrefillArgs &a, hipStream_t s) {
   using G_ = Geo<ET, DQK>;
@@ -566,15 +586,24 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t s) {
   const int T = kRows / Gc;
   const int n_qtiles = (a.max_q + T - 1) / T;
   const int64_t n_pairs = (int64_t)a.batch * a.num_heads_kv * head_chunks;
-  const int64_t blocks = (int64_t)kXcds * ((n_pairs + kXcds - 1) / kXcds) * n_qtiles;
+  const int64_t stream_bytes =
+      std::max<int64_t>((int64_t)a.max_kv * (DQK + kDvo) * ET::bytes, 1);
+#ifdef PKV_PREFILL_S
+  const int S = PKV_PREFILL_S;
+#else
+  int S = 1;
+  while (S < 8 && 2 * S * stream_bytes <= kStreamBytesPerXcd) S *= 2;
+#endif
+  const int64_t per_xcd = (n_pairs + kXcds - 1) / kXcds;
+  const int64_t blocks = (int64_t)kXcds * ((per_xcd + S - 1) / S) * S * n_qtiles;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (a.block_tables)
     hipLaunchKernelGGL((prefill_kernel<ET, DQK, OT, true>), dim3((uint32_t)blocks),
-                       dim3(kThreads), 0, s, a, T, Gc, head_chunks, n_qtiles);
+                       dim3(kThreads), 0, s, a, T, Gc, head_chunks, n_qtiles, S);
   else
     hipLaunchKernelGGL((prefill_kernel<ET, DQK, OT, false>), dim3((uint32_t)blocks),
-                       dim3(kThreads), 0, s, a, T, Gc, head_chunks, n_qtiles);
+                       dim3(kThreads), 0, s, a, T, Gc, head_chunks, n_qtiles, S);
   return hipGetLastError();
 }
 
