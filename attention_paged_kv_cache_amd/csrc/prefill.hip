@@ -17,11 +17,13 @@
 // Per kv tile of 64 keys
 //   K and V go from HBM straight into LDS with buffer_load_dwordx4 ... lds
 //   (no staging registers): each wave gathers 16 keys of the tile, all in
-//   one page, through the block table, with a buffer resource bounded to
-//   that page. Every DMA instruction is a full one (keys past the sequence
-//   end reload the last key; their scores are masked), so the loads carry
-//   no branches and are spread between the MFMAs of the previous tile
-//   instead of arriving as one burst. So that the 16 K rows one read
+//   one page, through the block table, with a buffer resource that starts
+//   at the wave's first key and ends at the sequence's last key. Every DMA
+//   instruction is a full one: lanes whose rows lie past the sequence end
+//   fall outside the resource and write zeros into LDS (their scores are
+//   masked). The loads carry no branches and no per-tile address math, and
+//   are spread between the MFMAs of the previous tile instead of arriving
+//   as one burst. So that the 16 K rows one read
 //   touches fall in distinct banks, 256-byte K rows (16-bit d 128) keep
 //   their 16-byte chunks XOR-swizzled by row (16 rows fill exactly 4 KB);
 //   other K rows are padded by 16 bytes, and each wave's 16 K rows occupy a
@@ -285,8 +287,6 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   const char *vbase = (const char *)a.v + (int64_t)kvh * a.head_stride_v * ES;
   const int64_t psk = a.page_stride_k * ES, psv = a.page_stride_v * ES;
   const int64_t ssk = a.slot_stride_k * ES, ssv = a.slot_stride_v * ES;
-  const int page_bytes_k = (int)((a.page_size - 1) * ssk + G_::ROWB);
-  const int page_bytes_v = (int)((a.page_size - 1) * ssv + G_::VRB);
 
   // Each wave gathers keys r0 .. r0+15 of every tile; they share one page
   // (page sizes 16, 32, 64). The page index is clamped into the sequence so
@@ -307,8 +307,8 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
 
   // Per-lane source rows / columns of each 1 KB LDS DMA of this wave's 16 K
   // rows (a whole number of KB per wave: lanes that fall in the row padding
-  // or past the 16th row load a valid duplicate into unused LDS bytes) and
-  // 16 V rows.
+  // or past the 16th row load a duplicate into unused LDS bytes) and 16 V
+  // rows.
   int k_row[G_::K_INSTR], k_col[G_::K_INSTR], v_row[G_::V_INSTR], v_col[G_::V_INSTR];
 #pragma unroll
   for (int q = 0; q < G_::K_INSTR; ++q) {
@@ -331,41 +331,42 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
     v_row[q] = row;
     v_col[q] = (pc ^ vswz<ES>(row)) * 16;
   }
-  // DMA state of the tile being loaded. Keys past the sequence end are
-  // loaded from the last key instead (finite data; their scores are masked,
-  // so their probabilities are exactly zero).
+  // DMA state of the tile being loaded: buffer resources over the wave's 16
+  // K and V rows, cut at the sequence end. Rows past it lie outside the
+  // range, and a buffer load out of range returns zeros, which the DMA
+  // writes into LDS like any other data (zero rows: their scores are masked
+  // and their probabilities are exactly zero, so they add nothing). The
+  // per-lane offsets inside the 16 rows are the same for every tile.
   struct Dma {
     __amdgpu_buffer_rsrc_t rk, rv;
-    int slot0, lim_row;
     char *kl, *vl;
   };
+  int k_off[G_::K_INSTR], v_off[G_::V_INSTR];
+#pragma unroll
+  for (int q = 0; q < G_::K_INSTR; ++q) k_off[q] = k_row[q] * (int)ssk + k_col[q];
+#pragma unroll
+  for (int q = 0; q < G_::V_INSTR; ++q) v_off[q] = v_row[q] * (int)ssv + v_col[q];
   auto dma_prep = [&](int j, int page, char *stage) {
     Dma d;
     const int key0 = j * kKeys + r0;
-    const bool in = key0 <= L_kv - 1;
+    const int valid = min(16, max(L_kv - key0, 0));  // rows inside the sequence
+    int64_t ok, ov;  // byte offsets of the block's first row
     if constexpr (PAGED) {
-      d.rk = make_rsrc(kbase + (int64_t)page * psk, page_bytes_k);
-      d.rv = make_rsrc(vbase + (int64_t)page * psv, page_bytes_v);
-      d.slot0 = in ? (key0 & ps_mask) : ((L_kv - 1) & ps_mask);
+      ok = (int64_t)page * psk + (int64_t)(key0 & ps_mask) * ssk;
+      ov = (int64_t)page * psv + (int64_t)(key0 & ps_mask) * ssv;
     } else {
-      const int key = in ? key0 : L_kv - 1;
-      d.rk = make_rsrc(kbase + (int64_t)(row_k + key) * ssk, (int)(15 * ssk + G_::ROWB));
-      d.rv = make_rsrc(vbase + (int64_t)(row_v + key) * ssv, (int)(15 * ssv + G_::VRB));
-      d.slot0 = 0;
+      ok = (int64_t)(row_k + key0) * ssk;
+      ov = (int64_t)(row_v + key0) * ssv;
     }
-    d.lim_row = in ? (L_kv - 1 - key0) : 0;
+    if (valid == 0) ok = ov = 0;
+    d.rk = make_rsrc(kbase + ok, valid > 0 ? (int)((valid - 1) * ssk + G_::ROWB) : 0);
+    d.rv = make_rsrc(vbase + ov, valid > 0 ? (int)((valid - 1) * ssv + G_::VRB) : 0);
     d.kl = stage + wave * G_::WKB;
     d.vl = stage + G_::K_BYTES + r0 * G_::VRB;
     return d;
   };
-  auto dma_k = [&](const Dma &d, int q) {
-    const int slot = d.slot0 + min(k_row[q], d.lim_row);
-    dma16b(d.rk, slot * (int)ssk + k_col[q], d.kl + q * 1024);
-  };
-  auto dma_v = [&](const Dma &d, int q) {
-    const int slot = d.slot0 + min(v_row[q], d.lim_row);
-    dma16b(d.rv, slot * (int)ssv + v_col[q], d.vl + q * 1024);
-  };
+  auto dma_k = [&](const Dma &d, int q) { dma16b(d.rk, k_off[q], d.kl + q * 1024); };
+  auto dma_v = [&](const Dma &d, int q) { dma16b(d.rv, v_off[q], d.vl + q * 1024); };
   auto issue_tile = [&](int j, int page, char *stage) {
     const Dma d = dma_prep(j, page, stage);
 #pragma unroll
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   auto tile_step = [&](int j, const char *cur, char *nxt) {
     const char *lds_k = cur;
     const char *lds_v = cur + G_::K_BYTES;
-    // Tile j + 1 (past the end: a harmless reload of the last key) is
+    // Tile j + 1 (past the end: zero-range loads that only write zeros) is
     // loaded into `nxt` by DMAs spread over this tile's MFMAs.
     const Dma dn = dma_prep(j + 1, pg_next, nxt);
 
@@ -503,8 +504,13 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
 
     // ---- P and O^T += V^T P^T, one 16-key k-step at a time ------------------
     // The exponentials of k-step k+1 run on the VALU while the MFMAs of
-    // k-step k execute. V^T comes from LDS transpose reads.
+    // k-step k execute. V^T comes from LDS transpose reads. The wave runs
+    // this phase at raised issue priority, so that a SIMD's arbiter serves a
+    // wave in its PV MFMA chain before waves in their softmax (e4m3 prefill
+    // 1341 -> 1385 TFLOP/s, bf16 unchanged; raised over the S^T phase or the
+    // softmax instead, it gained nothing).
     float psum = 0.0f;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kstep = 0; kstep < 4; ++kstep) {
       const int mb = kstep >> 1, hh = kstep & 1;
@@ -542,6 +548,7 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
         o[md] = mfma_pv(av, pb, o[md], PT{});
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     l_run += psum;
     // the page of tile j + 2 (read here, where its latency overlaps the wait)
     pg_next = wave_page(j + 2);
@@ -592,7 +599,6 @@ constexpr int64_t kStreamBytesPerXcd = (int64_t)3 << 20;
 
 template <class ET, int DQK, class OT>
 hipError_t launch_typed(const PrefillArgs &a, hipStream_t s) {
-  using G_ = Geo<ET, DQK>;
   const int G = a.num_heads_qo / a.num_heads_kv;
   const int Gc = G < kRows ? G : kRows;
   const int head_chunks = (G + Gc - 1) / Gc;
