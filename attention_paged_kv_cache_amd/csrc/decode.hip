@@ -17,12 +17,13 @@
 //   A unit is (request, kv head, split): `chunk` consecutive keys of the
 //   request's key range (only keys some query may see: with a window, the
 //   range starts at seq - q_len - window_left). A workgroup of 4 waves owns
-//   one unit; each wave streams chunk/4 keys, 32 at a time, straight from
-//   global memory into MFMA operands (no LDS on the streaming path):
-//     K: lane = (key, d run): 16-byte loads (8 d of one MFMA k-step, or
-//        16 e4m3 d feeding two k-steps, widened exactly to the query's
-//        16-bit type in registers).
-//     V: lane = (8 keys, 8-element d run): 16-byte loads (e4m3: a lane
+//   one unit; each wave streams chunk/4 keys, 32 at a time:
+//     K: 1 KB LDS DMAs of whole key rows into the wave's own LDS rows (two
+//        stages), then per lane = (key, d run) 16-byte operand reads (8 d
+//        of one MFMA k-step, or 16 e4m3 d feeding two k-steps, widened
+//        exactly to the query's 16-bit type in registers).
+//     V: lane = (8 keys, 8-element d run): 16-byte loads straight into
+//        registers (each load instruction reads whole rows; e4m3: a lane
 //        pair swaps halves to get there), then an 8x8 transpose in
 //        registers gives V^T operands whose k-run is 8 consecutive keys.
 //     S^T = K Q^T, online softmax in fp32 (base 2; the reference maximum
@@ -124,16 +125,46 @@ __device__ __forceinline__ void request_rows(const DecodeArgs &a, int b, int &ql
   }
 }
 
-// Raw K/V of one 32-key step as loaded (e4m3 bytes or 16-bit values).
+// Raw V of one 32-key step as loaded (e4m3 bytes or 16-bit values): 16-byte
+// loads either way, 8 keys x 8 d (16-bit), or 4 keys x 16 d (e4m3; the two
+// lanes of a pair swap halves to get 8 keys x 8 d each). K goes through LDS.
 template <bool FP8>
 struct RawKV {
-  // K: 16-byte loads either way: 8 d of one k-step (16-bit) or 16 d of two
-  // k-steps (e4m3), [m-block][load]
-  u32x4 k[2][FP8 ? 2 : 4];
-  // V, 16-byte loads either way: 8 keys x 8 d (16-bit), or 4 keys x 16 d
-  // (e4m3; the two lanes of a pair swap halves to get 8 keys x 8 d each)
   u32x4 v[FP8 ? 4 : 8];
 };
+
+// K of a 32-key step is staged in LDS, one wave's 32 rows in [row][d]
+// order. A K operand (16 rows x 16 bytes of d per lane group) read
+// straight from global memory touches 16 rows x 64 bytes per load
+// instruction, and such loads measured 5.66 TB/s against 6.73 for 1 KB
+// contiguous pieces (random 4 KB pages, same kernel shape). So each
+// 1 KB LDS DMA instead takes whole rows (4 rows of 256 B, or 8 of 128 B
+// for e4m3), and the operand is read back from LDS. The 16-byte chunk c of
+// row r sits at chunk slot c ^ kswz(r): the 16 rows one operand read
+// touches then fall in distinct banks.
+template <bool FP8>
+__device__ __forceinline__ int kswz(int row) {
+  return FP8 ? ((((row >> 3) << 1) | ((row >> 1) & 1)) & 7) : (((row >> 1) & 12) | (row & 3));
+}
+
+// Buffer resource over `bytes` bytes from `base` (raw, untyped access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, bytes, 0x00020000);
+}
+
+// 16 bytes from LDS (p points into a __shared__ array).
+__device__ __forceinline__ u32x4 lds16(const char *p) {
+  return *(const __attribute__((address_space(3))) u32x4 *)p;
+}
+
+// 16 bytes at rsrc + voff straight into LDS: lane l's bytes land at
+// lds_base + 16 * l (lds_base the same for every lane); STREAM: the
+// non-temporal cache policy. Loads past the resource's range write zeros.
+template <bool STREAM>
+__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, int voff, char *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base,
+                                           16, voff, 0, 0, STREAM ? 2 : 0);
+}
 
 // The value of the neighbouring lane (lane ^ 1) of a quad.
 __device__ __forceinline__ uint32_t swap_lane1(uint32_t x) {
@@ -166,6 +197,14 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
   // each row's draft mask as bits (bit i: draft i visible), when a mask is
   // given; read only on the steps that reach the drafts
   __shared__ uint64_t sh_mbits[R];
+  // each wave's K of a step, two stages (two arrays, so that the compiler
+  // sees that a DMA into one never aliases the reads of the other)
+  constexpr int KROWB = kD * ES;      // bytes of one K row
+  constexpr int LPR = KROWB / 16;     // DMA lanes per K row
+  constexpr int RPI = 64 / LPR;       // K rows per 1 KB DMA
+  constexpr int NKI = 32 / RPI;       // DMAs per step
+  __shared__ __attribute__((aligned(16))) char sk_a[kWaves][32 * KROWB];
+  __shared__ __attribute__((aligned(16))) char sk_b[kWaves][32 * KROWB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -296,7 +335,12 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
   pos_min = __builtin_amdgcn_readfirstlane(pos_min);
   wlo_max = __builtin_amdgcn_readfirstlane(wlo_max);
 
-  const int32_t *__restrict__ bt = a.block_tables + (int64_t)b * a.max_pages;
+  // block table row through the constant address space: scalar loads, so
+  // that the next step's page ids do not queue behind (and wait for) this
+  // step's K/V loads
+  const __attribute__((address_space(4))) int32_t *bt =
+      (const __attribute__((address_space(4))) int32_t *)(a.block_tables) +
+      (int64_t)b * a.max_pages;
   const int log2ps = __builtin_ctz(a.page_size);
   const int ps_mask = a.page_size - 1;
   const int last_pg = (seq - 1) >> log2ps;
@@ -313,6 +357,31 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
   koff[1] = koff[0] + 4;
   const int voff = 8 * g4;
 
+  // K DMA q, lane l: row q * RPI + l / LPR of the step, LDS chunk slot
+  // l % LPR, which holds global chunk slot ^ kswz(row). The row's offset in
+  // its page is taken modulo 16 for 16-token pages (rows 16..31 of a step
+  // are the second page's first 16). Loop invariant.
+  int kdma_off[NKI];
+#pragma unroll
+  for (int q = 0; q < NKI; ++q) {
+    const int row = q * RPI + lane / LPR;
+    const int c = (lane % LPR) ^ kswz<FP8>(row);
+    kdma_off[q] = (row & (a.page_size == 16 ? 15 : 31)) * (int)sstr + c * 16;
+  }
+  // a page's rows of this kv head (the resource's range)
+  const int kpage_bytes = (int)((a.page_size - 1) * sstr + KROWB);
+  // operand reads: m-block mb, 16-byte piece u (16-bit: k-step u; e4m3:
+  // k-steps 2u and 2u + 1) of the lane's key row koff[mb]
+  constexpr int KU = FP8 ? 2 : 4;
+  int kld[2][KU];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int row = koff[mb];
+      kld[mb][u] = wave * (32 * KROWB) + row * KROWB + ((4 * u + g4) ^ kswz<FP8>(row)) * 16;
+    }
+
   // The two pages a 32-key step can touch (the second differs only for
   // 16-token pages); indices are clamped into the sequence so that no
   // padding entry of the block table is ever followed.
@@ -320,30 +389,40 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
     p0 = bt[min(kg0 >> log2ps, last_pg)];
     p1 = bt[min((kg0 + 16) >> log2ps, last_pg)];
   };
-  auto issue = [&](RawKV<FP8> &r, int kg0, int p0, int p1) {
-    const char *kb0 = kbase + (int64_t)p0 * psk, *kb1 = kbase + (int64_t)p1 * psk;
-    const char *vb0 = vbase + (int64_t)p0 * psv, *vb1 = vbase + (int64_t)p1 * psv;
+  // Loads of one step. Every step issues the next one unconditionally, so
+  // that the compiler's wait before a step's compute counts exactly the
+  // next step's loads (a conditional issue left a join at which it waited
+  // for all loads). Past the wave's last step (live = false) the K DMAs get
+  // an empty range (no memory access; they write zeros into the unused
+  // stage) and the V loads all read the same 256 bytes of the query.
+  auto issue = [&](RawKV<FP8> &r, int kg0, int p0, int p1, char *stage, bool live) {
+    // K: NKI DMAs of RPI whole rows each into this wave's LDS rows; the
+    // rows of one DMA lie in one page (RPI divides 16)
+    const int64_t kin = (int64_t)(kg0 & ps_mask) * sstr;  // step's first row in its page
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int off = koff[mb];
-      const char *kp = ((off >> log2ps) ? kb1 : kb0) + ((kg0 + off) & ps_mask) * sstr;
-#pragma unroll
-      for (int u = 0; u < (FP8 ? 2 : 4); ++u)
-        r.k[mb][u] = ld16_kv<STREAM>(kp + kstep_d<FP8>(FP8 ? 2 * u : u, g4) * ES);
+    for (int q = 0; q < NKI; ++q) {
+      const int p = ((q * RPI) >> log2ps) ? p1 : p0;
+      dma16b<STREAM>(make_rsrc(kbase + (int64_t)p * psk + kin, live ? kpage_bytes : 0),
+                     kdma_off[q], stage + wave * (32 * KROWB) + q * 1024);
     }
+    const char *vb0 = vbase + (int64_t)p0 * psv, *vb1 = vbase + (int64_t)p1 * psv;
+    const int64_t vstr = live ? sstr : 0;
+    const char *vdummy = (const char *)a.q + (lane & 15) * 16;
     if constexpr (FP8) {
       // lane pair (2i, 2i+1): d 16i..16i+15, keys 0-3 (even) / 4-7 (odd)
       // of the pair's 8-key group
       const int vo = voff + 4 * (r16 & 1);
       const char *vp =
           ((vo >> log2ps) ? vb1 : vb0) + ((kg0 + vo) & ps_mask) * sstr + (r16 >> 1) * 16;
+      if (!live) vp = vdummy;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) r.v[jj] = ld16_kv<STREAM>(vp + jj * sstr);
+      for (int jj = 0; jj < 4; ++jj) r.v[jj] = ld16_kv<STREAM>(vp + jj * vstr);
     } else {
       const char *vp =
           ((voff >> log2ps) ? vb1 : vb0) + ((kg0 + voff) & ps_mask) * sstr + r16 * 8 * ES;
+      if (!live) vp = vdummy;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) r.v[jj] = ld16_kv<STREAM>(vp + jj * sstr);
+      for (int jj = 0; jj < 8; ++jj) r.v[jj] = ld16_kv<STREAM>(vp + jj * vstr);
     }
   };
 
@@ -359,7 +438,7 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
     l_run[nb] = 0.0f;
   }
 
-  auto compute = [&](const RawKV<FP8> &r, int kg0) {
+  auto compute = [&](const RawKV<FP8> &r, int kg0, const char *stage) {
     // ---- S^T = K Q^T (e4m3 K widened one k-step at a time, right before
     // its MFMAs; V is widened and transposed after the softmax, so neither
     // holds registers across the other's work) --------------------------------
@@ -374,10 +453,10 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
       for (int s = 0; s < 4; ++s) {
         u32x4 kop;
         if constexpr (FP8) {
-          const u32x4 w = r.k[mb][s >> 1];
+          const u32x4 w = lds16(stage + kld[mb][s >> 1]);
           kop = widen8((s & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]}, QT{});
         } else {
-          kop = r.k[mb][s];
+          kop = lds16(stage + kld[mb][s]);
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) sacc[mb][nb] = mfma16(kop, qop[nb][s], sacc[mb][nb], QT{});
@@ -486,27 +565,35 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
     RawKV<FP8> buf_a, buf_b;
     int p0, p1, n0, n1;
     step_pages(w_begin, p0, p1);
-    issue(buf_a, w_begin, p0, p1);
+    issue(buf_a, w_begin, p0, p1, &sk_a[0][0], true);
     step_pages(w_begin + 32, n0, n1);
+    // The first step's loads land before the loop. The compiler's waits
+    // are static: with these loads still pending on the loop's entry path
+    // (whose registers differ from the back edge's), the loop head waited
+    // for every outstanding load on every iteration.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     int kg = w_begin;
     while (true) {
       bool more = kg + 32 < w_end;
-      if (more) {
-        issue(buf_b, kg + 32, n0, n1);
-        step_pages(kg + 64, n0, n1);
-      }
-      compute(buf_a, kg);
+      issue(buf_b, kg + 32, n0, n1, &sk_b[0][0], more);
+      step_pages(kg + 64, n0, n1);
+      // keep this step's first LDS reads (and so their wait) after the next
+      // step's loads are issued
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf_a, kg, &sk_a[0][0]);
       kg += 32;
       if (!more) break;
       more = kg + 32 < w_end;
-      if (more) {
-        issue(buf_a, kg + 32, n0, n1);
-        step_pages(kg + 64, n0, n1);
-      }
-      compute(buf_b, kg);
+      issue(buf_a, kg + 32, n0, n1, &sk_a[0][0], more);
+      step_pages(kg + 64, n0, n1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf_b, kg, &sk_b[0][0]);
       kg += 32;
       if (!more) break;
     }
+    // the last, empty issue's DMAs write LDS: drain them before the
+    // workgroup can end
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 
   // ---- merge the four waves ------------------------------------------------------
