@@ -468,20 +468,24 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
                        (kg0 + 31 <= pos_min) && (kg0 + 32 <= mask_from);
     if (!clean) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int nb = 0; nb < NB; ++nb) {
+        // the row's draft bits, read once (no load inside the per-key
+        // selects, so they stay branch-free)
+        const uint64_t bits = a.mask ? sh_mbits[nb * 16 + r16] : ~0ull;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = kg0 + 8 * g4 + 4 * mb + i;
             // a draft key (key >= mask_from, so 0 <= key - dstart < ql for
             // keys inside the sequence) must have its mask bit set
             const uint32_t di = (uint32_t)(key - dstart);
-            const bool hidden = key >= mask_from &&
-                                !(di < 64u && ((sh_mbits[nb * 16 + r16] >> di) & 1ull));
+            const bool shown = di < 64u && ((bits >> (di & 63)) & 1ull);
+            const bool hidden = key >= mask_from && !shown;
             if (key >= w_end || key < w_begin || key > pos[nb] || key < wlo[nb] || hidden)
               sacc[mb][nb][i] = -INFINITY;
           }
+      }
     }
 
     // ---- online softmax per row ----------------------------------------------
@@ -572,24 +576,35 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
     // (whose registers differ from the back edge's), the loop head waited
     // for every outstanding load on every iteration.
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    int kg = w_begin;
-    while (true) {
-      bool more = kg + 32 < w_end;
-      issue(buf_b, kg + 32, n0, n1, &sk_b[0][0], more);
+    // Steps go in pairs (buffers a then b), with the loop's only exit at
+    // its test: a second exit after the first step of a pair became a path
+    // from that step back to the loop head in the compiler's structured
+    // control flow, on which the first step's loads were pending, so the
+    // loop head waited for every load. An odd last pair skips its second
+    // compute (its loads were the empty ones).
+    const int n_steps = (w_end - w_begin + 31) >> 5;
+    // Before a step's compute, wait until only the next step's loads (NKI
+    // DMAs and NV V loads, issued after this step's) are outstanding: the
+    // wait for this step's K DMAs (LDS writes) is explicit rather than left
+    // to the compiler, whose tracking of DMA writes into LDS dropped it
+    // across the loop's back edge.
+    constexpr int NV = FP8 ? 4 : 8;
+    constexpr int kWaitStep = NKI + NV;
+    constexpr int kWaitImm = 0x0F70 | (kWaitStep & 15) | ((kWaitStep >> 4) << 14);
+    for (int i = 0; i < n_steps; i += 2) {
+      const int kg = w_begin + 32 * i;
+      issue(buf_b, kg + 32, n0, n1, &sk_b[0][0], i + 1 < n_steps);
       step_pages(kg + 64, n0, n1);
-      // keep this step's first LDS reads (and so their wait) after the next
-      // step's loads are issued
+      __builtin_amdgcn_s_waitcnt(kWaitImm);
+      // nothing crosses: this step's LDS reads stay after the wait, the
+      // next step's loads before it
       __builtin_amdgcn_sched_barrier(0);
       compute(buf_a, kg, &sk_a[0][0]);
-      kg += 32;
-      if (!more) break;
-      more = kg + 32 < w_end;
-      issue(buf_a, kg + 32, n0, n1, &sk_a[0][0], more);
-      step_pages(kg + 64, n0, n1);
+      issue(buf_a, kg + 64, n0, n1, &sk_a[0][0], i + 2 < n_steps);
+      step_pages(kg + 96, n0, n1);
+      __builtin_amdgcn_s_waitcnt(kWaitImm);
       __builtin_amdgcn_sched_barrier(0);
-      compute(buf_b, kg, &sk_b[0][0]);
-      kg += 32;
-      if (!more) break;
+      if (i + 1 < n_steps) compute(buf_b, kg + 32, &sk_b[0][0]);
     }
     // the last, empty issue's DMAs write LDS: drain them before the
     // workgroup can end
