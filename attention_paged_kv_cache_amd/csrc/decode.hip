@@ -22,10 +22,10 @@
 //        stages), then per lane = (key, d run) 16-byte operand reads (8 d
 //        of one MFMA k-step, or 16 e4m3 d feeding two k-steps, widened
 //        exactly to the query's 16-bit type in registers).
-//     V: lane = (8 keys, 8-element d run): 16-byte loads straight into
-//        registers (each load instruction reads whole rows; e4m3: a lane
-//        pair swaps halves to get there), then an 8x8 transpose in
-//        registers gives V^T operands whose k-run is 8 consecutive keys.
+//     V: lane = (8 keys, 8-element d run): 16-byte (e4m3: 8-byte) loads
+//        straight into registers, each load instruction reading whole
+//        rows, then an 8x8 transpose in registers gives V^T operands whose
+//        k-run is 8 consecutive keys.
 //     S^T = K Q^T, online softmax in fp32 (base 2; the reference maximum
 //     is raised lazily, so most steps skip rescaling O), O^T += V^T P^T.
 //   With one row group per unit the K/V loads are non-temporal (streaming):
@@ -69,7 +69,6 @@ __device__ __forceinline__ u32x4 widen8(u32x2 w, BF16Tag) {
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 __device__ __forceinline__ u32x4 widen8(u32x2 w, F16Tag) {
-  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
   u32x4 r;
   r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, false));
   r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[0], 1.0f, true));
@@ -125,13 +124,25 @@ __device__ __forceinline__ void request_rows(const DecodeArgs &a, int b, int &ql
   }
 }
 
-// Raw V of one 32-key step as loaded (e4m3 bytes or 16-bit values): 16-byte
-// loads either way, 8 keys x 8 d (16-bit), or 4 keys x 16 d (e4m3; the two
-// lanes of a pair swap halves to get 8 keys x 8 d each). K goes through LDS.
+// Raw V of one 32-key step as loaded: 8 keys x 8 d per lane, as 16-byte
+// loads of 16-bit values (v) or 8-byte loads of e4m3 bytes (v8); each load
+// instruction reads whole rows (4 rows). Loading e4m3 V 16 bytes per lane
+// (4 keys x 16 d) and swapping halves between the lanes of a pair issued
+// half the loads but cost a DPP move and selects per dword: speculative
+// decode 5.87 vs 5.93 TB/s once K went through LDS. K goes through LDS.
 template <bool FP8>
 struct RawKV {
-  u32x4 v[FP8 ? 4 : 8];
+  u32x4 v[FP8 ? 1 : 8];
+  u32x2 v8[FP8 ? 8 : 1];
 };
+
+template <bool STREAM>
+__device__ __forceinline__ u32x2 ld8_kv(const void *p) {
+  if constexpr (STREAM)
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+  else
+    return ld8(p);
+}
 
 // K of a 32-key step is staged in LDS, one wave's 32 rows in [row][d]
 // order. A K operand (16 rows x 16 bytes of d per lane group) read
@@ -164,11 +175,6 @@ template <bool STREAM>
 __device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, int voff, char *lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base,
                                            16, voff, 0, 0, STREAM ? 2 : 0);
-}
-
-// The value of the neighbouring lane (lane ^ 1) of a quad.
-__device__ __forceinline__ uint32_t swap_lane1(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
 }
 
 // d offset of the 8 query elements lane group g4 feeds to k-step t. For
@@ -409,14 +415,12 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
     const int64_t vstr = live ? sstr : 0;
     const char *vdummy = (const char *)a.q + (lane & 15) * 16;
     if constexpr (FP8) {
-      // lane pair (2i, 2i+1): d 16i..16i+15, keys 0-3 (even) / 4-7 (odd)
-      // of the pair's 8-key group
-      const int vo = voff + 4 * (r16 & 1);
+      // keys voff .. voff+7, d 8*r16 .. 8*r16+7 (8 bytes of each row)
       const char *vp =
-          ((vo >> log2ps) ? vb1 : vb0) + ((kg0 + vo) & ps_mask) * sstr + (r16 >> 1) * 16;
+          ((voff >> log2ps) ? vb1 : vb0) + ((kg0 + voff) & ps_mask) * sstr + r16 * 8;
       if (!live) vp = vdummy;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) r.v[jj] = ld16_kv<STREAM>(vp + jj * vstr);
+      for (int jj = 0; jj < 8; ++jj) r.v8[jj] = ld8_kv<STREAM>(vp + jj * vstr);
     } else {
       const char *vp =
           ((voff >> log2ps) ? vb1 : vb0) + ((kg0 + voff) & ps_mask) * sstr + r16 * 8 * ES;
@@ -533,15 +537,8 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
       // each lane keeps the 8 d of its own d-run and sends the other 8 to
       // its partner: even lanes end with keys 0-3 loaded and 4-7 received,
       // odd lanes the reverse
-      const bool odd = r16 & 1;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const u32x4 w = r.v[jj];
-        const u32x2 own = odd ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
-        const u32x2 got = {swap_lane1(odd ? w[0] : w[2]), swap_lane1(odd ? w[1] : w[3])};
-        vrow[jj] = widen8(odd ? got : own, QT{});
-        vrow[4 + jj] = widen8(odd ? own : got, QT{});
-      }
+      for (int jj = 0; jj < 8; ++jj) vrow[jj] = widen8(r.v8[jj], QT{});
     } else {
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) vrow[jj] = r.v[jj];
@@ -588,7 +585,7 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
     // wait for this step's K DMAs (LDS writes) is explicit rather than left
     // to the compiler, whose tracking of DMA writes into LDS dropped it
     // across the loop's back edge.
-    constexpr int NV = FP8 ? 4 : 8;
+    constexpr int NV = 8;  // V loads per step
     constexpr int kWaitStep = NKI + NV;
     constexpr int kWaitImm = 0x0F70 | (kWaitStep & 15) | ((kWaitStep >> 4) << 14);
     for (int i = 0; i < n_steps; i += 2) {
