@@ -199,7 +199,6 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
   constexpr int R = NB * 16;
   __shared__ float sh_m[kWaves][R];
   __shared__ float sh_l[kWaves][R];
-  __shared__ float sh_o[R][kD + 4];
   // each row's draft mask as bits (bit i: draft i visible), when a mask is
   // given; read only on the steps that reach the drafts
   __shared__ uint64_t sh_mbits[R];
@@ -209,8 +208,14 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
   constexpr int LPR = KROWB / 16;     // DMA lanes per K row
   constexpr int RPI = 64 / LPR;       // K rows per 1 KB DMA
   constexpr int NKI = 32 / RPI;       // DMAs per step
-  __shared__ __attribute__((aligned(16))) char sk_a[kWaves][32 * KROWB];
-  __shared__ __attribute__((aligned(16))) char sk_b[kWaves][32 * KROWB];
+  // The four waves' O^T are merged after the loop in sh_o, which reuses the
+  // first K stage: every wave has left the loop (and drained its DMAs) by
+  // the merge's first barrier.
+  constexpr int KSTAGE = kWaves * 32 * KROWB;
+  constexpr int SHO = R * (kD + 4) * 4;
+  __shared__ __attribute__((aligned(16))) char sk_a[KSTAGE > SHO ? KSTAGE : SHO];
+  __shared__ __attribute__((aligned(16))) char sk_b[KSTAGE];
+  float(*sh_o)[kD + 4] = reinterpret_cast<float(*)[kD + 4]>(sk_a);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -374,8 +379,19 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
     const int c = (lane % LPR) ^ kswz<FP8>(row);
     kdma_off[q] = (row & (a.page_size == 16 ? 15 : 31)) * (int)sstr + c * 16;
   }
-  // a page's rows of this kv head (the resource's range)
+  // With 16-bit K the resources end at the sequence's last key: rows past
+  // it load zeros (their scores are masked) and cost no memory traffic
+  // (batch decode 6.36 -> 6.42 TB/s). The e4m3 kernel, bound by its
+  // instruction stream rather than by its loads, measured slower with the
+  // per-DMA bound (5.93 vs 5.88 TB/s) and maps the whole page. rows_from:
+  // the step's rows before this DMA's page part (16 for the second page of
+  // a 16-token page step).
   const int kpage_bytes = (int)((a.page_size - 1) * sstr + KROWB);
+  auto dma_bytes = [&](int kg0, int rows_from, bool live) {
+    if constexpr (FP8) return live ? kpage_bytes : 0;
+    const int n = live ? min(32, seq - kg0 - rows_from) : 0;
+    return n > 0 ? (int)((n - 1) * sstr + KROWB) : 0;
+  };
   // operand reads: m-block mb, 16-byte piece u (16-bit: k-step u; e4m3:
   // k-steps 2u and 2u + 1) of the lane's key row koff[mb]
   constexpr int KU = FP8 ? 2 : 4;
@@ -407,8 +423,9 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
     const int64_t kin = (int64_t)(kg0 & ps_mask) * sstr;  // step's first row in its page
 #pragma unroll
     for (int q = 0; q < NKI; ++q) {
-      const int p = ((q * RPI) >> log2ps) ? p1 : p0;
-      dma16b<STREAM>(make_rsrc(kbase + (int64_t)p * psk + kin, live ? kpage_bytes : 0),
+      const bool second = (q * RPI) >> log2ps;
+      const int p = second ? p1 : p0;
+      dma16b<STREAM>(make_rsrc(kbase + (int64_t)p * psk + kin, dma_bytes(kg0, second ? 16 : 0, live)),
                      kdma_off[q], stage + wave * (32 * KROWB) + q * 1024);
     }
     const char *vb0 = vbase + (int64_t)p0 * psv, *vb1 = vbase + (int64_t)p1 * psv;
@@ -534,9 +551,6 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
     // ---- O^T += V^T P^T --------------------------------------------------------
     u32x4 vrow[8];
     if constexpr (FP8) {
-      // each lane keeps the 8 d of its own d-run and sends the other 8 to
-      // its partner: even lanes end with keys 0-3 loaded and 4-7 received,
-      // odd lanes the reverse
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) vrow[jj] = widen8(r.v8[jj], QT{});
     } else {
@@ -566,7 +580,7 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
     RawKV<FP8> buf_a, buf_b;
     int p0, p1, n0, n1;
     step_pages(w_begin, p0, p1);
-    issue(buf_a, w_begin, p0, p1, &sk_a[0][0], true);
+    issue(buf_a, w_begin, p0, p1, sk_a, true);
     step_pages(w_begin + 32, n0, n1);
     // The first step's loads land before the loop. The compiler's waits
     // are static: with these loads still pending on the loop's entry path
@@ -590,18 +604,18 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
     constexpr int kWaitImm = 0x0F70 | (kWaitStep & 15) | ((kWaitStep >> 4) << 14);
     for (int i = 0; i < n_steps; i += 2) {
       const int kg = w_begin + 32 * i;
-      issue(buf_b, kg + 32, n0, n1, &sk_b[0][0], i + 1 < n_steps);
+      issue(buf_b, kg + 32, n0, n1, sk_b, i + 1 < n_steps);
       step_pages(kg + 64, n0, n1);
       __builtin_amdgcn_s_waitcnt(kWaitImm);
       // nothing crosses: this step's LDS reads stay after the wait, the
       // next step's loads before it
       __builtin_amdgcn_sched_barrier(0);
-      compute(buf_a, kg, &sk_a[0][0]);
-      issue(buf_a, kg + 64, n0, n1, &sk_a[0][0], i + 2 < n_steps);
+      compute(buf_a, kg, sk_a);
+      issue(buf_a, kg + 64, n0, n1, sk_a, i + 2 < n_steps);
       step_pages(kg + 96, n0, n1);
       __builtin_amdgcn_s_waitcnt(kWaitImm);
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 1 < n_steps) compute(buf_b, kg + 32, &sk_b[0][0]);
+      if (i + 1 < n_steps) compute(buf_b, kg + 32, sk_b);
     }
     // the last, empty issue's DMAs write LDS: drain them before the
     // workgroup can end
