@@ -56,15 +56,25 @@ __global__ void csr_to_block_tables_kernel(const int32_t *__restrict__ indptr,
   bt[(int64_t)b * max_pages + k] = k < n ? indices[start + k] : -1;
 }
 
-// One thread per (row, pair of 16-byte chunks): it resolves the row's page
-// once (batch index -> position -> page id through kv_indptr/kv_indices,
-// and the slot) and moves the pair's bytes of both K and V, so four 16-byte
-// loads are in flight behind one lookup. Chunk c and c + half of a row go
-// to one thread, so consecutive threads read consecutive 16-byte pieces of
-// the appended rows and write consecutive pieces of each head's run. A
-// chunk is 16 bytes of one head's head_dim run, so a write never straddles
-// a head (or a page slot) in either layout.
-constexpr int kAppendChunks = 2;
+// One thread per (row, group of C 16-byte chunks): it resolves the row's
+// page once (batch index -> position -> page id through
+// kv_indptr/kv_indices, and the slot) and moves the group's bytes of both K
+// and V, so 2C 16-byte loads are in flight behind one lookup. Chunks
+// c, c + groups, ... of a row go to one thread, so consecutive threads read
+// consecutive 16-byte pieces of the appended rows and write consecutive
+// pieces of each head's run. A chunk is 16 bytes of one head's head_dim
+// run, so a write never straddles a head (or a page slot) in either layout.
+//
+// C by layout (TB/s by C = 1 / 2 / 4 / 8, one MI355X, same process):
+//   HND, e4m3 1 KB rows:  5.43 / 5.49 / 5.65 / 5.64
+//   HND, fp16 2 KB rows:  5.64 / 5.54 / 5.77 / 5.48
+//   NHD, e4m3 1 KB rows:  5.88 / 5.90 / 5.74 / 5.23
+//   NHD, fp16 8 KB rows:  5.75 / 5.31 / 5.42 / 5.25
+// A token's heads are adjacent in NHD (one contiguous run per row): many
+// threads of one chunk each stream it best. In HND each head's run goes to
+// its own place in the page, and four chunks per thread do best.
+constexpr int kChunksHnd = 4;
+constexpr int kChunksNhd = 1;
 
 // Bytes of appended rows (K and V) from which the append streams: the
 // chip's 256 MB last-level cache.
@@ -72,7 +82,7 @@ constexpr int64_t kAppendStreamBytes = (int64_t)256 << 20;
 
 // NTL / NTS: non-temporal (streaming) loads of the appended rows / stores
 // into the pages.
-template <bool NTL, bool NTS>
+template <bool NTL, bool NTS, int C>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a, int32_t chunks_per_head,
                                                      int32_t chunks_per_row, int32_t groups,
                                                      int64_t total) {
@@ -88,9 +98,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a, int32_t chunk
   const char *vs = (const char *)a.value + row * chunks_per_row * 16;
   char *kd = (char *)a.k_cache + (int64_t)page * a.page_stride_k + slot;
   char *vd = (char *)a.v_cache + (int64_t)page * a.page_stride_v + slot;
-  u32x4 kv[2][kAppendChunks];
+  u32x4 kv[2][C];
 #pragma unroll
-  for (int u = 0; u < kAppendChunks; ++u) {
+  for (int u = 0; u < C; ++u) {
     const int32_t c = g + u * groups;
     if (c < chunks_per_row) {
       if constexpr (NTL) {
@@ -103,7 +113,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a, int32_t chunk
     }
   }
 #pragma unroll
-  for (int u = 0; u < kAppendChunks; ++u) {
+  for (int u = 0; u < C; ++u) {
     const int32_t c = g + u * groups;
     if (c < chunks_per_row) {
       const int32_t head = c / chunks_per_head;
@@ -173,11 +183,10 @@ hipError_t launch_csr_to_block_tables(const int32_t *indptr,
   return hipGetLastError();
 }
 
-hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
-  if (a.nnz == 0) return hipSuccess;
-  const int32_t chunks_per_head = a.row_bytes_per_head / 16;
-  const int32_t chunks_per_row = chunks_per_head * a.num_heads;
-  const int32_t groups = (chunks_per_row + kAppendChunks - 1) / kAppendChunks;
+template <int C>
+static void launch_append_c(const AppendArgs &a, int32_t chunks_per_head, int32_t chunks_per_row,
+                            hipStream_t s) {
+  const int32_t groups = (chunks_per_row + C - 1) / C;
   const int64_t total = (int64_t)a.nnz * groups;
   const int64_t blocks = (total + 255) / 256;
   // Appends that read at least kAppendStreamBytes of rows use non-temporal
@@ -190,11 +199,22 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
   // measured 6.26 -> 5.40 TB/s).
   const int64_t src_bytes = 2 * (int64_t)a.nnz * chunks_per_row * 16;
   if (src_bytes >= kAppendStreamBytes)
-    hipLaunchKernelGGL((append_kernel<true, true>), dim3((uint32_t)blocks), dim3(256), 0, s, a,
+    hipLaunchKernelGGL((append_kernel<true, true, C>), dim3((uint32_t)blocks), dim3(256), 0, s, a,
                        chunks_per_head, chunks_per_row, groups, total);
   else
-    hipLaunchKernelGGL((append_kernel<false, false>), dim3((uint32_t)blocks), dim3(256), 0, s, a,
-                       chunks_per_head, chunks_per_row, groups, total);
+    hipLaunchKernelGGL((append_kernel<false, false, C>), dim3((uint32_t)blocks), dim3(256), 0, s,
+                       a, chunks_per_head, chunks_per_row, groups, total);
+}
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
+  if (a.nnz == 0) return hipSuccess;
+  const int32_t chunks_per_head = a.row_bytes_per_head / 16;
+  const int32_t chunks_per_row = chunks_per_head * a.num_heads;
+  // NHD: a slot's heads are adjacent (the head stride is one head's run)
+  if (a.head_stride == a.row_bytes_per_head)
+    launch_append_c<kChunksNhd>(a, chunks_per_head, chunks_per_row, s);
+  else
+    launch_append_c<kChunksHnd>(a, chunks_per_head, chunks_per_row, s);
   return hipGetLastError();
 }
 
