@@ -66,22 +66,22 @@ __global__ __launch_bounds__(256) void read_stream_kernel(const u32x4 *__restric
 }
 
 // Each workgroup copies its own contiguous span of per_wg16 16-byte vectors
-// from src to dst, kReadUnroll loads in flight per thread before their
-// stores; NT selects non-temporal (streaming) loads and stores.
-template <bool NT>
+// from src to dst, U loads in flight per thread before their stores; NT
+// selects non-temporal (streaming) loads and stores.
+template <bool NT, int U>
 __global__ __launch_bounds__(256) void copy_stream_kernel(const u32x4 *__restrict__ src,
                                                           u32x4 *__restrict__ dst,
                                                           int64_t per_wg16) {
   const int64_t base = (int64_t)blockIdx.x * per_wg16 + threadIdx.x;
   const u32x4 *q = src + base;
   u32x4 *d = dst + base;
-  for (int64_t i = 0; i < per_wg16; i += 256 * kReadUnroll) {
-    u32x4 v[kReadUnroll];
+  for (int64_t i = 0; i < per_wg16; i += 256 * U) {
+    u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u)
+    for (int u = 0; u < U; ++u)
       v[u] = NT ? __builtin_nontemporal_load(q + i + 256 * u) : q[i + 256 * u];
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       if (NT)
         __builtin_nontemporal_store(v[u], d + i + 256 * u);
       else
@@ -120,24 +120,31 @@ CEIL_API int pkv_ceiling_read(const void *buf, int64_t bytes, int32_t blocks, ui
 }
 
 // Copies `bytes` from `src` to `dst` (both 16-byte aligned, not
-// overlapping; bytes a multiple of blocks * 32 KiB, each workgroup taking an
-// equal contiguous span), with non-temporal loads and stores when
-// `nontemporal` is nonzero.
+// overlapping; bytes a multiple of blocks * unroll * 4 KiB, each workgroup
+// taking an equal contiguous span), `unroll` (4 or 8) 16-byte loads in
+// flight per thread, with non-temporal loads and stores when `nontemporal`
+// is nonzero.
 CEIL_API int pkv_ceiling_copy(const void *src, void *dst, int64_t bytes, int32_t blocks,
-                              int32_t nontemporal, void *stream) {
-  const int64_t span = (int64_t)blocks * 256 * kReadUnroll * 16;
+                              int32_t nontemporal, int32_t unroll, void *stream) {
+  if (unroll != 4 && unroll != 8) return (int)hipErrorInvalidValue;
+  const int64_t span = (int64_t)blocks * 256 * unroll * 16;
   if (blocks <= 0 || bytes <= 0 || bytes % span || src == nullptr || dst == nullptr ||
       (uintptr_t)src % 16 || (uintptr_t)dst % 16)
     return (int)hipErrorInvalidValue;
   const char *s = (const char *)src;
   const char *d = (const char *)dst;
   if (s < d + bytes && d < s + bytes) return (int)hipErrorInvalidValue;
-  if (nontemporal)
-    hipLaunchKernelGGL(copy_stream_kernel<true>, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
-                       (const u32x4 *)src, (u32x4 *)dst, bytes / 16 / blocks);
+  const int64_t per = bytes / 16 / blocks;
+  const hipStream_t st = (hipStream_t)stream;
+  const u32x4 *si = (const u32x4 *)src;
+  u32x4 *di = (u32x4 *)dst;
+  if (nontemporal && unroll == 8)
+    hipLaunchKernelGGL((copy_stream_kernel<true, 8>), dim3(blocks), dim3(256), 0, st, si, di, per);
+  else if (nontemporal)
+    hipLaunchKernelGGL((copy_stream_kernel<true, 4>), dim3(blocks), dim3(256), 0, st, si, di, per);
+  else if (unroll == 8)
+    hipLaunchKernelGGL((copy_stream_kernel<false, 8>), dim3(blocks), dim3(256), 0, st, si, di, per);
   else
-    hipLaunchKernelGGL(copy_stream_kernel<false>, dim3(blocks), dim3(256), 0,
-                       (hipStream_t)stream, (const u32x4 *)src, (u32x4 *)dst,
-                       bytes / 16 / blocks);
+    hipLaunchKernelGGL((copy_stream_kernel<false, 4>), dim3(blocks), dim3(256), 0, st, si, di, per);
   return (int)hipGetLastError();
 }

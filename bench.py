@@ -425,32 +425,41 @@ def measured_ceilings(torch, steps=10):
     del x, y
 
     # hand-written streaming copy of 512 MiB (the bulk append's read and
-    # write sizes), plain and non-temporal loads and stores
+    # write sizes): plain and non-temporal loads and stores, 4 or 8 loads in
+    # flight per thread, 2048 or 8192 workgroups; the fastest is the ceiling
     lib.pkv_ceiling_copy.restype = ctypes.c_int
     lib.pkv_ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
-    cbytes, cblocks = 512 << 20, 2048
+                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_void_p]
+    cbytes = 512 << 20
     src = torch.empty(cbytes, dtype=torch.uint8, device=dev).fill_(3)
     dst = torch.empty_like(src)
     kcopy = {}
     for nt in (0, 1):
-        t = time_steps(lambda: ok(lib.pkv_ceiling_copy(src.data_ptr(), dst.data_ptr(), cbytes,
-                                                       cblocks, nt, stream), "copy stream"),
-                       steps, 3)
-        kcopy[nt] = 2 * cbytes / (t.median_ms * 1e-3) / 1e9
+        for unroll in (4, 8):
+            for cblocks in (2048, 8192):
+                t = time_steps(lambda: ok(lib.pkv_ceiling_copy(src.data_ptr(), dst.data_ptr(),
+                                                               cbytes, cblocks, nt, unroll,
+                                                               stream), "copy stream"),
+                               steps, 3)
+                kcopy[(nt, unroll, cblocks)] = 2 * cbytes / (t.median_ms * 1e-3) / 1e9
     del src, dst
     torch.cuda.empty_cache()
+    best = max(kcopy, key=kcopy.get)
     return {"mfma_bf16_loop_TFLOPs": round(mfma, 1), "hbm_read_4GiB_GBs": round(read, 1),
             "hbm_copy_1GiB_GBs": round(copy, 1),
-            "hbm_copy_kernel_512MiB_GBs": round(max(kcopy.values()), 1),
-            "hbm_copy_kernel_plain_GBs": round(kcopy[0], 1),
-            "hbm_copy_kernel_nontemporal_GBs": round(kcopy[1], 1),
+            "hbm_copy_kernel_512MiB_GBs": round(kcopy[best], 1),
+            "hbm_copy_kernel_best": {"nontemporal": bool(best[0]), "loads_per_thread": best[1],
+                                     "workgroups": best[2]},
+            "hbm_copy_kernel_plain_GBs": round(max(v for k, v in kcopy.items() if not k[0]), 1),
+            "hbm_copy_kernel_nontemporal_GBs": round(max(v for k, v in kcopy.items() if k[0]), 1),
             "what": "pure v_mfma_f32_32x32x16_bf16 loop (8 chains per wave, 8192 waves); "
                     "non-temporal 16-byte loads over 4 GiB (2048 workgroups, one contiguous "
                     "span each); torch copy_ of 1 GiB (read + write counted); a hand-written "
-                    "copy of 512 MiB (2048 workgroups, one contiguous span each, 8 loads of 16 "
-                    "bytes in flight per thread before their stores; plain and non-temporal, "
-                    "the faster reported; read + write counted); medians of 10 calls"}
+                    "copy of 512 MiB (one contiguous span per workgroup, 4 or 8 loads of 16 "
+                    "bytes in flight per thread before their stores, 2048 or 8192 workgroups, "
+                    "plain or non-temporal: the fastest of the eight reported, its shape in "
+                    "hbm_copy_kernel_best; read + write counted); medians of 10 calls"}
 
 
 def _cpu_cores(torch):

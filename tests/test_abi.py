@@ -211,3 +211,12 @@ def test_ceiling_library_exports_and_validates():
     assert c.pkv_ceiling_read(dummy, 4 * 32768, 4, None, None) != 0
     assert c.pkv_ceiling_mfma_bf16(0, 1, dummy, None) != 0
     assert c.pkv_ceiling_mfma_bf16(1, 1, None, None) != 0
+    c.pkv_ceiling_copy.restype = ctypes.c_int
+    c.pkv_ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p]
+    dst = ctypes.c_void_p(1 << 30)
+    assert c.pkv_ceiling_copy(dummy, dst, 4 * 16384, 4, 1, 3, None) != 0  # unroll 4 or 8
+    assert c.pkv_ceiling_copy(dummy, dst, 1000, 4, 1, 4, None) != 0       # span
+    assert c.pkv_ceiling_copy(dummy, dummy, 4 * 16384, 4, 1, 4, None) != 0  # overlap
+    assert c.pkv_ceiling_copy(ctypes.c_void_p(4100), dst, 4 * 16384, 4, 1, 4, None) != 0
