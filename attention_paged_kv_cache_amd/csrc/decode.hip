@@ -77,8 +77,9 @@ __device__ __forceinline__ u32x4 widen8(u32x2 w, F16Tag) {
   return r;
 }
 
-// K/V loads. With one row group per unit every K/V byte is read once per
-// call, and non-temporal (streaming) loads measured faster than plain ones
+// K/V loads (V loads, and the cache policy of the K DMAs). With one row
+// group per unit every K/V byte is read once per call, and non-temporal
+// (streaming) loads measured faster than plain ones
 // (bit-identical outputs; batch decode 5.74 -> 5.82 TB/s, speculative decode
 // (e4m3) 5.12 -> 5.77 TB/s, 5.18 -> 5.61 with cold caches). With several row
 // groups the later groups re-read the unit's K/V from L2, which streaming
@@ -90,16 +91,6 @@ __device__ __forceinline__ u32x4 ld16_kv(const void *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
   else
     return ld16(p);
-}
-
-// Load 8 consecutive d elements of one key row as a 16-byte operand.
-template <bool FP8, class QT>
-__device__ __forceinline__ u32x4 load_run(const char *p) {
-  if constexpr (FP8) {
-    return widen8(ld8(p), QT{});
-  } else {
-    return ld16(p);
-  }
 }
 
 // First key a unit range may start at: the window's left edge (if any),
@@ -178,8 +169,8 @@ __device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, int voff, char 
 }
 
 // d offset of the 8 query elements lane group g4 feeds to k-step t. For
-// e4m3 K a lane loads 16 consecutive d (one 16-byte load) and feeds its two
-// halves to k-steps 2u and 2u + 1; Q uses the same assignment. Any
+// e4m3 K a lane reads 16 consecutive d (one 16-byte LDS read) and feeds its
+// two halves to k-steps 2u and 2u + 1; Q uses the same assignment. Any
 // assignment that covers every d once per kv head gives the same dot
 // product.
 template <bool FP8>
