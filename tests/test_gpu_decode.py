@@ -63,6 +63,27 @@ def test_layouts_and_pages(pkv, ps, layout):
     check(pkv, small(page_size=ps, layout=layout, seed=ps))
 
 
+@pytest.mark.parametrize("ps,layout,kv", [(16, "HND", "bf16"), (16, "NHD", "e4m3"),
+                                          (32, "NHD", "bf16"), (32, "HND", "e4m3"),
+                                          (64, "HND", "bf16"), (64, "NHD", "e4m3")])
+@pytest.mark.parametrize("ql,hqo,hkv", [(1, 8, 2), (4, 16, 2)])
+def test_steps_per_wave(pkv, ps, layout, kv, ql, hqo, hkv):
+    # One plan for the batch (its chunk, 640 keys here, comes from the
+    # longest request), so each wave streams 0 to 5 32-key steps: odd and
+    # even counts (steps go in pairs; an odd last pair skips its second
+    # compute), a partial last step, waves with no keys, and sequence ends
+    # in either half of a 16-token page (whose second half is another page).
+    lens = [max(ql, 1), 20, 33, 64, 95, 130, 161, 300, 371, 517]
+    kv_dtype = torch.float8_e4m3fn if kv == "e4m3" else torch.bfloat16
+    w = workloads.batch_decode(device=DEV, seed=70 + ps + ql, batch=len(lens), seq=(517, 517),
+                               num_qo_heads=hqo, num_kv_heads=hkv, page_size=ps,
+                               q_len_per_req=ql, kv_dtype=kv_dtype, layout=layout)
+    w["seq_lens"] = torch.tensor(lens, dtype=torch.uint32)
+    w["max_seq_len"] = max(lens)
+    assert pkv.decode_workspace_size(len(lens), ql, hqo, hkv, 128, max(lens), -1) == 0
+    check(pkv, w)
+
+
 def test_long_sequences_split_kv(pkv):
     # long enough that every request needs several splits
     check(pkv, small(batch=3, seq=(3000, 9000), seed=41))
