@@ -158,7 +158,7 @@ def test_append_then_decode_step_replays(pkv):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        # the replay wrote this round's rows at each request's last 4 positions
+        # the replay wrote this replay's rows at each request's last 4 positions
         for b in (0, 5):
             L = int(w["seq_lens"][b])
             for r in range(4):
