@@ -573,11 +573,6 @@ __global__ __launch_bounds__(kThreads, (NB == 1 || FP8) ? 2 : 1) void decode_ker
     step_pages(w_begin, p0, p1);
     issue(buf_a, w_begin, p0, p1, sk_a, true);
     step_pages(w_begin + 32, n0, n1);
-    // The first step's loads land before the loop. The compiler's waits
-    // are static: with these loads still pending on the loop's entry path
-    // (whose registers differ from the back edge's), the loop head waited
-    // for every outstanding load on every iteration.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
     // Steps go in pairs (buffers a then b), with the loop's only exit at
     // its test: a second exit after the first step of a pair became a path
     // from that step back to the loop head in the compiler's structured
