@@ -15,7 +15,8 @@ on the host for comparison.
 Rates come from warm back-to-back calls; each leg also reports the median of
 calls made after a 1 GiB read has evicted the caches ("flushed"). The
 speculative step and the append page's Example (append then causal fp16
-prefill, launch-bound) are also timed as a captured HIP graph. The measured
+prefill, launch-bound) are also timed as captured HIP graphs, of one step
+and of 8 steps back to back (per-step figures). The measured
 ceilings (a pure MFMA loop, a streaming read, copies) put the rates beside
 what this GPU reaches at all. The float64 oracle is timed on a bounded
 sample of every workload (cpu_baseline; its "configs" holds each one).
@@ -121,6 +122,10 @@ def _stats(per, region_ms):
 # than 10 warm-up calls of the short workloads. Settling first makes every
 # leg a steady-state measurement.
 SETTLE_MS = 250.0
+
+# Steps captured in one HIP graph for the multi-step graph timings of the
+# launch-bound steps.
+GRAPH_STEPS = 8
 
 
 def settle(fn):
@@ -356,10 +361,13 @@ def bench_example(pkv, torch, workloads):
     return w, flops, abytes, step, append, prefill
 
 
-def time_graph(torch, fn, steps, warmup):
-    """The same timing as time_steps for `fn` captured once in a HIP graph and
-    replayed: what the step costs on the GPU without the host's per-call
-    argument handling and launch gaps."""
+def time_graph(torch, fn, steps, warmup, per_graph=1):
+    """The same timing as time_steps for `per_graph` calls of `fn` captured
+    once in a HIP graph and replayed: what the step costs on the GPU without
+    the host's per-call argument handling and launch gaps. With per_graph > 1
+    one replay runs that many steps back to back (a serving loop's steps in
+    one graph), and every figure is divided by per_graph: the per-replay
+    launch cost is then shared by those steps."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -369,11 +377,12 @@ def time_graph(torch, fn, steps, warmup):
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        fn()
+        for _ in range(per_graph):
+            fn()
     torch.cuda.synchronize()
     t = time_steps(g.replay, steps, warmup)
     del g
-    return t
+    return Timing(*(x / per_graph for x in t))
 
 
 # ---- measured ceilings -------------------------------------------------------------
@@ -719,6 +728,8 @@ def main():
     f5d = time_flushed(decode5, args.steps, flush)
     t5g = time_graph(torch, step5, args.steps, args.warmup)
     t5ag = time_graph(torch, append5, args.steps, args.warmup)
+    t5g8 = time_graph(torch, step5, args.steps, args.warmup, GRAPH_STEPS)
+    t5ag8 = time_graph(torch, append5, args.steps, args.warmup, GRAPH_STEPS)
     if cpu:
         print("bench: float64 oracle, speculative step sample", file=sys.stderr, flush=True)
         reqs = list(range(16))
@@ -745,6 +756,7 @@ def main():
     t0a = time_steps(append0, args.steps, args.warmup)
     t0p = time_steps(prefill0, args.steps, args.warmup)
     t0g = time_graph(torch, step0, args.steps, args.warmup)
+    t0g8 = time_graph(torch, step0, args.steps, args.warmup, GRAPH_STEPS)
     if cpu:
         print("bench: float64 oracle, append example", file=sys.stderr, flush=True)
         base["append_example"] = cpu_example(w)
@@ -824,6 +836,7 @@ def main():
                         "sinks, q_len_per_req 4",
             "ms_per_step": round(t5.region_ms, 4),
             "graph_ms_per_step": round(t5g.region_ms, 4),
+            f"graph{GRAPH_STEPS}_ms_per_step": round(t5g8.region_ms, 4),
             "decode_value": round(d5_l, 1), "unit": "GB/s",
             "decode_bytes": bytes5,
             "roofline": roofline("hbm", d5_l, PEAK_HBM_GBS, "GB/s",
@@ -831,6 +844,7 @@ def main():
             "decode": timing(t5d, f5d, bytes5, G),
             "append_ms": round(t5a.launch_ms, 4),
             "append_graph_ms": round(t5ag.launch_ms, 4),
+            f"append_graph{GRAPH_STEPS}_ms": round(t5ag8.launch_ms, 4),
             "append_GBs": round(rate(abytes5, t5a.launch_ms, G), 1),
             "append_roofline": roofline("hbm", rate(abytes5, t5ag.launch_ms, G), PEAK_HBM_GBS,
                                         "GB/s", traffic("append_spec_e4m3", APPEND_SRC)),
@@ -852,6 +866,7 @@ def main():
                         "get_batch_indices_positions, append, csr_to_block_tables, prefill",
             "us_per_step": round(t0s.region_ms * 1e3, 2),
             "graph_us_per_step": round(t0g.region_ms * 1e3, 2),
+            f"graph{GRAPH_STEPS}_us_per_step": round(t0g8.region_ms * 1e3, 2),
             "us_median": round(t0s.median_ms * 1e3, 2), "us_min": round(t0s.min_ms * 1e3, 2),
             "append_us": round(t0a.launch_ms * 1e3, 2),
             "prefill_us": round(t0p.launch_ms * 1e3, 2),
@@ -904,14 +919,25 @@ def only(args, torch, pkv, workloads):
         w, nb, ab, append, decode = bench_spec(pkv, torch, workloads)
         td = time_steps(decode, args.steps, args.warmup)
         ta = time_steps(append, args.steps, args.warmup)
+        def step():
+            append()
+            decode()
+
+        tg = time_graph(torch, step, args.steps, args.warmup)
+        tg8 = time_graph(torch, step, args.steps, args.warmup, GRAPH_STEPS)
         r = {"decode GB/s": rate(nb, td.launch_ms, G), "ms_decode": td.launch_ms,
-             "ms_append": ta.launch_ms}
+             "ms_append": ta.launch_ms, "graph_ms_per_step": tg.region_ms,
+             f"graph{GRAPH_STEPS}_ms_per_step": tg8.region_ms}
     elif args.only == "ceilings":
         r = measured_ceilings(torch)
     elif args.only == "example":
         w, flops0, abytes0, step0, _, _ = bench_example(pkv, torch, workloads)
         t = time_steps(step0, args.steps, args.warmup)
-        r = {"us_per_step": t.region_ms * 1e3, "us_median": t.median_ms * 1e3}
+        tg = time_graph(torch, step0, args.steps, args.warmup)
+        tg8 = time_graph(torch, step0, args.steps, args.warmup, GRAPH_STEPS)
+        r = {"us_per_step": t.region_ms * 1e3, "us_median": t.median_ms * 1e3,
+             "graph_us_per_step": tg.region_ms * 1e3,
+             f"graph{GRAPH_STEPS}_us_per_step": tg8.region_ms * 1e3}
     else:  # append_sweep
         flush = new_flush_buffer(torch)
         for k in range(12, 21):
