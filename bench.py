@@ -141,28 +141,35 @@ def settle(fn):
 
 
 def time_steps(fn, steps, warmup):
-    """Warm caches: settle (see SETTLE_MS), `warmup` untimed calls, then `steps`
-    calls back to back.
-    region_ms is the whole region per step; launch/min/median_ms come from
-    events around each call. Events sit on the current stream, which is the
-    stream the library enqueues on."""
+    """Warm caches: settle (see SETTLE_MS), `warmup` untimed calls, then two
+    timed passes of `steps` calls back to back.
+    region_ms: the first pass, with events only at its two ends, per step.
+    launch/min/median_ms: the second pass, from events around each call.
+    Each event pair on the GPU's timeline adds about 5 us to the call it
+    brackets (the kernel trace's durations are that much shorter), so the
+    rates come from region_ms and the per-call figures give the spread.
+    Events sit on the current stream, which is the stream the library
+    enqueues on."""
     import torch
     settle(fn)
     for _ in range(warmup):
         fn()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    region = start.elapsed_time(end) / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
     for a, b in ev:
         a.record()
         fn()
         b.record()
-    end.record()
     torch.cuda.synchronize()
-    return _stats([a.elapsed_time(b) for a, b in ev], start.elapsed_time(end) / steps)
+    return _stats([a.elapsed_time(b) for a, b in ev], region)
 
 
 def new_flush_buffer(torch):
@@ -388,9 +395,10 @@ def time_graph(torch, fn, steps, warmup, per_graph=1):
 # ---- measured ceilings -------------------------------------------------------------
 
 def measured_ceilings(torch, steps=10):
-    """Rates of a pure bf16 MFMA loop, a streaming 4 GiB read and a 1 GiB
-    device copy on this GPU (libpkv_ceiling.so), each the median of `steps`
-    timed calls after warm-up."""
+    """Rates of a pure bf16 MFMA loop, a streaming 4 GiB read, a 1 GiB
+    device copy and a hand-written 512 MiB copy on this GPU
+    (libpkv_ceiling.so), each over `steps` back-to-back calls after warm-up,
+    timed as the workloads are (region_ms)."""
     path = os.path.join(ROOT, "attention_paged_kv_cache_amd", "libpkv_ceiling.so")
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build first "
@@ -415,7 +423,7 @@ def measured_ceilings(torch, steps=10):
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     t = time_steps(lambda: ok(lib.pkv_ceiling_mfma_bf16(blocks, iters, out.data_ptr(), stream),
                               "mfma loop"), steps, 3)
-    mfma = lib.pkv_ceiling_mfma_bf16_flop(blocks, iters) / (t.median_ms * 1e-3) / 1e12
+    mfma = lib.pkv_ceiling_mfma_bf16_flop(blocks, iters) / (t.region_ms * 1e-3) / 1e12
     del out
 
     nbytes, rblocks = 4 << 30, 2048
@@ -424,13 +432,13 @@ def measured_ceilings(torch, steps=10):
     t = time_steps(lambda: ok(lib.pkv_ceiling_read(buf.data_ptr(), nbytes, rblocks,
                                                    words.data_ptr(), stream), "read stream"),
                    steps, 3)
-    read = nbytes / (t.median_ms * 1e-3) / 1e9
+    read = nbytes / (t.region_ms * 1e-3) / 1e9
     del buf, words
 
     x = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
     y = torch.empty_like(x)
     t = time_steps(lambda: y.copy_(x), steps, 3)
-    copy = 2 * x.numel() * 4 / (t.median_ms * 1e-3) / 1e9
+    copy = 2 * x.numel() * 4 / (t.region_ms * 1e-3) / 1e9
     del x, y
 
     # hand-written streaming copy of 512 MiB (the bulk append's read and
@@ -451,7 +459,7 @@ def measured_ceilings(torch, steps=10):
                                                                cbytes, cblocks, nt, unroll,
                                                                stream), "copy stream"),
                                steps, 3)
-                kcopy[(nt, unroll, cblocks)] = 2 * cbytes / (t.median_ms * 1e-3) / 1e9
+                kcopy[(nt, unroll, cblocks)] = 2 * cbytes / (t.region_ms * 1e-3) / 1e9
     del src, dst
     torch.cuda.empty_cache()
     best = max(kcopy, key=kcopy.get)
@@ -468,7 +476,8 @@ def measured_ceilings(torch, steps=10):
                     "copy of 512 MiB (one contiguous span per workgroup, 4 or 8 loads of 16 "
                     "bytes in flight per thread before their stores, 2048 or 8192 workgroups, "
                     "plain or non-temporal: the fastest of the eight reported, its shape in "
-                    "hbm_copy_kernel_best; read + write counted); medians of 10 calls"}
+                    "hbm_copy_kernel_best; read + write counted); each over 10 "
+                    "back-to-back calls"}
 
 
 def _cpu_cores(torch):
@@ -777,11 +786,11 @@ def main():
                             "value": round(rate(work, f.median_ms, scale), 1)}
         return d
 
-    p_l = rate(flops, t1.launch_ms, T)
-    p3_l = rate(flops3, t3.launch_ms, T)
-    d4_l = rate(bytes4, t4.launch_ms, G)
-    d5_l = rate(bytes5, t5d.launch_ms, G)
-    a6_l = rate(bytes6, t6.launch_ms, G)
+    p_l = rate(flops, t1.region_ms, T)
+    p3_l = rate(flops3, t3.region_ms, T)
+    d4_l = rate(bytes4, t4.region_ms, G)
+    d5_l = rate(bytes5, t5d.region_ms, G)
+    a6_l = rate(bytes6, t6.region_ms, G)
     mixed = mixed_fp8_peak(192, 128)
     line = {
         "metric": METRIC,
@@ -842,11 +851,11 @@ def main():
             "roofline": roofline("hbm", d5_l, PEAK_HBM_GBS, "GB/s",
                                  traffic("spec_decode_e4m3", DECODE_SRC)),
             "decode": timing(t5d, f5d, bytes5, G),
-            "append_ms": round(t5a.launch_ms, 4),
-            "append_graph_ms": round(t5ag.launch_ms, 4),
-            f"append_graph{GRAPH_STEPS}_ms": round(t5ag8.launch_ms, 4),
-            "append_GBs": round(rate(abytes5, t5a.launch_ms, G), 1),
-            "append_roofline": roofline("hbm", rate(abytes5, t5ag.launch_ms, G), PEAK_HBM_GBS,
+            "append_ms": round(t5a.region_ms, 4),
+            "append_graph_ms": round(t5ag.region_ms, 4),
+            f"append_graph{GRAPH_STEPS}_ms": round(t5ag8.region_ms, 4),
+            "append_GBs": round(rate(abytes5, t5a.region_ms, G), 1),
+            "append_roofline": roofline("hbm", rate(abytes5, t5ag8.region_ms, G), PEAK_HBM_GBS,
                                         "GB/s", traffic("append_spec_e4m3", APPEND_SRC)),
         },
         "bulk_append": {
@@ -868,10 +877,10 @@ def main():
             "graph_us_per_step": round(t0g.region_ms * 1e3, 2),
             f"graph{GRAPH_STEPS}_us_per_step": round(t0g8.region_ms * 1e3, 2),
             "us_median": round(t0s.median_ms * 1e3, 2), "us_min": round(t0s.min_ms * 1e3, 2),
-            "append_us": round(t0a.launch_ms * 1e3, 2),
-            "prefill_us": round(t0p.launch_ms * 1e3, 2),
-            "append_GBs": round(rate(abytes0, t0a.launch_ms, G), 1),
-            "prefill_TFLOPs": round(rate(flops0, t0p.launch_ms, T), 3),
+            "append_us": round(t0a.region_ms * 1e3, 2),
+            "prefill_us": round(t0p.region_ms * 1e3, 2),
+            "append_GBs": round(rate(abytes0, t0a.region_ms, G), 1),
+            "prefill_TFLOPs": round(rate(flops0, t0p.region_ms, T), 3),
             "bound": "launch latency (3.3 MB moved, 27 MFLOP)",
         },
     }
@@ -900,21 +909,25 @@ def only(args, torch, pkv, workloads):
         x = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
         y = torch.empty_like(x)
         t = time_steps(lambda: y.copy_(x), args.steps, args.warmup)
-        r = {"GB/s": rate(2 * x.numel() * 4, t.launch_ms, G), "bytes_read": x.numel() * 4,
-             "bytes_written": x.numel() * 4, "ms_launch": t.launch_ms}
+        r = {"GB/s": rate(2 * x.numel() * 4, t.region_ms, G), "bytes_read": x.numel() * 4,
+             "bytes_written": x.numel() * 4, "ms_per_step": t.region_ms,
+             "ms_launch": t.launch_ms}
     elif args.only in ("prefill", "fp8prefill"):
         w, flops, step = bench_prefill(pkv, torch, workloads, fp8=args.only == "fp8prefill")
         t = time_steps(step, args.steps, args.warmup)
-        r = {"TFLOP/s": rate(flops, t.launch_ms, T), "ms_launch": t.launch_ms,
+        r = {"TFLOP/s": rate(flops, t.region_ms, T), "ms_per_step": t.region_ms,
+             "ms_launch": t.launch_ms,
              "ms_min": t.min_ms}
     elif args.only == "append":
         bytes6, step = bench_append(pkv, torch, workloads.bulk_append("cuda:0"))
         t = time_steps(step, args.steps, args.warmup)
-        r = {"GB/s": rate(bytes6, t.launch_ms, G), "ms_launch": t.launch_ms, "ms_min": t.min_ms}
+        r = {"GB/s": rate(bytes6, t.region_ms, G), "ms_per_step": t.region_ms,
+             "ms_launch": t.launch_ms, "ms_min": t.min_ms}
     elif args.only == "decode":
         w, nb, step = bench_decode(pkv, torch, workloads)
         t = time_steps(step, args.steps, args.warmup)
-        r = {"GB/s": rate(nb, t.launch_ms, G), "ms_launch": t.launch_ms, "ms_min": t.min_ms}
+        r = {"GB/s": rate(nb, t.region_ms, G), "ms_per_step": t.region_ms,
+             "ms_launch": t.launch_ms, "ms_min": t.min_ms}
     elif args.only == "spec":
         w, nb, ab, append, decode = bench_spec(pkv, torch, workloads)
         td = time_steps(decode, args.steps, args.warmup)
@@ -925,8 +938,9 @@ def only(args, torch, pkv, workloads):
 
         tg = time_graph(torch, step, args.steps, args.warmup)
         tg8 = time_graph(torch, step, args.steps, args.warmup, GRAPH_STEPS)
-        r = {"decode GB/s": rate(nb, td.launch_ms, G), "ms_decode": td.launch_ms,
-             "ms_append": ta.launch_ms, "graph_ms_per_step": tg.region_ms,
+        r = {"decode GB/s": rate(nb, td.region_ms, G), "ms_decode": td.region_ms,
+             "ms_decode_launch": td.launch_ms, "ms_append": ta.region_ms,
+             "graph_ms_per_step": tg.region_ms,
              f"graph{GRAPH_STEPS}_ms_per_step": tg8.region_ms}
     elif args.only == "ceilings":
         r = measured_ceilings(torch)
