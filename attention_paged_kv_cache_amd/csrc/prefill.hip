@@ -176,7 +176,6 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
   using G_ = Geo<ET, DQK>;
   using PT = typename PvTag<ET>::type;
   constexpr int ES = G_::ES;
-  constexpr bool kVEarly = ES == 2;  // next tile's V DMAs in the S^T phase
   // Two LDS stages of [K rows | V rows]: tile j is read from one while tile
   // j + 1 lands in the other. Two distinct arrays (not one buffer indexed by
   // j % 2) let the compiler see that the DMA into one stage never aliases
@@ -446,15 +445,14 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
       }
 #pragma unroll
       for (int q = 0; q < G_::K_INSTR; ++q) dma_k(dn, q);
-      // 16-bit inputs also issue the next tile's V DMAs here, among this
-      // tile's S^T MFMAs (the V stage they fill was last read before the
-      // previous barrier): they then have the whole tile to land before the
-      // end-of-tile wait (bf16 974 -> 1004 TFLOP/s, bit-identical). With
-      // e4m3 the S^T phase is six MFMAs, and the V DMAs stay in the PV phase.
-      if constexpr (kVEarly) {
+      // The next tile's V DMAs are issued here too, among this tile's S^T
+      // MFMAs (the V stage they fill was last read before the previous
+      // barrier): they then have the whole tile to land before the
+      // end-of-tile wait. Bit-identical outputs; bf16 974 -> 1004 TFLOP/s
+      // against issuing them in the PV phase, e4m3 (six S^T MFMAs) 1378 ->
+      // 1393 and 1401 -> 1405 on two boxes.
 #pragma unroll
-        for (int q = 0; q < G_::V_INSTR; ++q) dma_v(dn, q);
-      }
+      for (int q = 0; q < G_::V_INSTR; ++q) dma_v(dn, q);
       constexpr int kRd = G_::KB / 16;             // LDS reads per MFMA
       constexpr int kMf = 2 * G_::KSTEPS;          // MFMAs
       constexpr int kAhead = 2;                    // MFMAs of look-ahead
@@ -463,7 +461,7 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
       for (int i = 0; i < kMf - kAhead; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
-        if (i % 2 == 1 && i / 2 < G_::K_INSTR + (kVEarly ? G_::V_INSTR : 0))
+        if (i % 2 == 1 && i / 2 < G_::K_INSTR + G_::V_INSTR)
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
@@ -514,13 +512,6 @@ __global__ __launch_bounds__(kThreads, (DQK * ET::bytes > 256) ? 1 : 2) void pre
 #pragma unroll
     for (int kstep = 0; kstep < 4; ++kstep) {
       const int mb = kstep >> 1, hh = kstep & 1;
-      if constexpr (!kVEarly) {
-        if (kstep < G_::V_INSTR) dma_v(dn, kstep);
-        if (kstep == 3) {
-#pragma unroll
-          for (int q = 4; q < G_::V_INSTR; ++q) dma_v(dn, q);
-        }
-      }
       u32x4 pb;
 #pragma unroll
       for (int w2 = 0; w2 < 4; ++w2) {
