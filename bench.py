@@ -19,9 +19,11 @@ prefill, launch-bound) are also timed as captured HIP graphs, of one step
 and of 8 steps back to back (per-step figures). The measured
 ceilings (a pure MFMA loop, a streaming read, copies) put the rates beside
 what this GPU reaches at all. The float64 oracle is timed on a bounded
-sample of every workload (cpu_baseline; its "configs" holds each one).
+sample of every workload (cpu_baseline; its "configs" holds each one). An
+append scaling sweep (2^12 to 2^20 rows of the append Example's shape) closes
+the line.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-sweep]
        python bench.py --only {prefill,fp8prefill,decode,spec,append,copy,ceilings,append_sweep,
                                example}
 """
@@ -59,6 +61,8 @@ def parse():
                    help="untimed back-to-back calls of each workload for at least this long "
                         "before its warm-up steps (0: none; profiling runs pass 0)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the append scaling sweep")
     p.add_argument("--no-flush", action="store_true",
                    help="skip the cold-cache timings and the measured ceilings (kernel traces)")
     p.add_argument("--only", choices=["prefill", "decode", "spec", "fp8prefill", "append", "copy",
@@ -326,6 +330,34 @@ def bench_append(pkv, torch, w):
 
     elem = w["k_append"].element_size()
     return append_bytes(nnz, w["num_kv_heads"], w["head_dim"], elem), step
+
+
+# nnz of the append scaling sweep: the append Example's shape family (fp16, 32
+# kv heads, d 128, NHD page 16) from 2^12 to 2^20 rows, an extra measurement
+# (not one of the workloads) that shows whether the scatter itself is bound
+# by HBM bandwidth, which the workloads' small appends cannot show.
+SWEEP_NNZ = [1 << k for k in range(12, 21)]
+
+
+def bench_append_sweep(pkv, torch, workloads, steps, warmup, flush, nnzs=SWEEP_NNZ):
+    """Warm (region) and flushed (per-call median) rates of the append at each
+    nnz of `nnzs`; one dict per size."""
+    G = 1e9
+    points = []
+    for nnz in nnzs:
+        w = workloads.append_sweep("cuda:0", nnz=nnz)
+        nb, step = bench_append(pkv, torch, w)
+        t = time_steps(step, steps, warmup)
+        f = time_flushed(step, steps, flush)
+        pt = {"nnz": nnz, "bytes": nb, "GB/s": round(rate(nb, t.region_ms, G), 1),
+              "ms_per_step": round(t.region_ms, 4)}
+        if f is not None:
+            pt["flushed_GB/s"] = round(rate(nb, f.median_ms, G), 1)
+            pt["flushed_ms_median"] = round(f.median_ms, 4)
+        points.append(pt)
+        del w, step
+        torch.cuda.empty_cache()
+    return points
 
 
 def bench_example(pkv, torch, workloads):
@@ -770,6 +802,13 @@ def main():
         print("bench: float64 oracle, append example", file=sys.stderr, flush=True)
         base["append_example"] = cpu_example(w)
     del w, step0, append0, prefill0
+    torch.cuda.empty_cache()
+
+    sweep = None
+    if not args.no_sweep:
+        print("bench: append scaling sweep (fp16, NHD, 2^12 to 2^20 rows)", file=sys.stderr,
+              flush=True)
+        sweep = bench_append_sweep(pkv, torch, workloads, args.steps, args.warmup, flush)
     flush = None
     torch.cuda.empty_cache()
 
@@ -884,6 +923,16 @@ def main():
             "bound": "launch latency (3.3 MB moved, 27 MFLOP)",
         },
     }
+    if sweep is not None:
+        line["append_sweep"] = {
+            "what": "extra measurement, not a workload: the append Example's shape family "
+                    "(fp16, 32 kv heads, d 128, NHD page 16), each request appending its "
+                    "whole sequence into its own pages in random order, nnz from 2^12 to "
+                    "2^20 rows; bytes = rows read + rows written + indices; GB/s over the "
+                    "timed region (back to back), flushed_GB/s the median of calls after a "
+                    "1 GiB read",
+            "points": sweep,
+        }
     if ceil is not None:
         line["measured_ceilings"] = {
             **ceil,
@@ -954,18 +1003,8 @@ def only(args, torch, pkv, workloads):
              f"graph{GRAPH_STEPS}_us_per_step": tg8.region_ms * 1e3}
     else:  # append_sweep
         flush = new_flush_buffer(torch)
-        for k in range(12, 21):
-            w = workloads.append_sweep("cuda:0", nnz=1 << k)
-            nb, step = bench_append(pkv, torch, w)
-            t = time_steps(step, args.steps, args.warmup)
-            f = time_flushed(step, args.steps, flush)
-            print(json.dumps({"only": "append_sweep", "nnz": 1 << k, "bytes": nb,
-                              "GB/s": round(rate(nb, t.median_ms, G), 1),
-                              "flushed GB/s": round(rate(nb, f.median_ms, G), 1),
-                              "ms_median": round(t.median_ms, 4),
-                              "ms_flushed_median": round(f.median_ms, 4)}), flush=True)
-            del w, step
-            torch.cuda.empty_cache()
+        for pt in bench_append_sweep(pkv, torch, workloads, args.steps, args.warmup, flush):
+            print(json.dumps({"only": "append_sweep", **pt}), flush=True)
         return
     print(json.dumps({"only": args.only,
                       **{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}}),
