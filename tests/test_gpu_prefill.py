@@ -96,6 +96,26 @@ def test_page_sizes_and_nhd(pkv, ps):
                              num_kv_heads=2, dtype=torch.float16, pool_pages=200))
 
 
+@pytest.mark.parametrize("hqo,hkv,dtype,d_qk", [
+    (9, 3, torch.bfloat16, 128),        # group 3: 42 tokens x 3 heads per 128-row tile
+    (10, 2, torch.bfloat16, 128),       # group 5: 25 tokens, rows 125-127 unused
+    (12, 2, torch.float8_e4m3fn, 192),  # group 6: 21 tokens, 192-byte rows
+    (24, 2, torch.float8_e4m3fn, 128),  # group 12: 10 tokens, 128-byte rows
+    (12, 1, torch.float16, 192),        # group 12, 384-byte rows
+    (130, 1, torch.bfloat16, 128),      # group 130: two head chunks (128 + 2), 1 token
+])
+def test_row_groups(pkv, hqo, hkv, dtype, d_qk):
+    """Query tiles whose 128 rows pack a number of tokens that is not a power
+    of two (or heads spread over two workgroups): the row -> (token, head)
+    mapping of the Q operands and of the output rows, unused rows included,
+    against the oracle over several ragged query tiles."""
+    small = hqo > 64
+    w = small_prefill(seed=60 + hqo, num_qo_heads=hqo, num_kv_heads=hkv, dtype=dtype,
+                      d_qk=d_qk, batch=2 if small else 3, q_len=(1, 40 if small else 130),
+                      prefix=(0, 30 if small else 100))
+    check(pkv, w)
+
+
 def test_d192_bf16(pkv):
     check(pkv, small_prefill(d_qk=192, num_qo_heads=8, num_kv_heads=4, seed=7))
 
