@@ -4,6 +4,7 @@ rejects bad arguments on the host before any HIP call (no GPU needed)."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -220,3 +221,29 @@ def test_ceiling_library_exports_and_validates():
     assert c.pkv_ceiling_copy(dummy, dst, 1000, 4, 1, 4, None) != 0       # span
     assert c.pkv_ceiling_copy(dummy, dummy, 4 * 16384, 4, 1, 4, None) != 0  # overlap
     assert c.pkv_ceiling_copy(ctypes.c_void_p(4100), dst, 4 * 16384, 4, 1, 4, None) != 0
+
+
+def test_header_compiles_as_c99_and_cpp17(tmp_path):
+    """include/pkv.h is a plain C header (C99, pedantic, warnings as errors)
+    and the same text compiles as C++17."""
+    for cc, std, lang in (("gcc", "-std=c99", "c"), ("g++", "-std=c++17", "c++")):
+        r = subprocess.run([cc, std, "-Wall", "-Wextra", "-Werror", "-pedantic",
+                            "-fsyntax-only", "-x", lang, HEADER],
+                           capture_output=True, text=True, timeout=120)
+        assert r.returncode == 0, r.stderr
+
+
+def test_c_program_links_and_gets_statuses(lib, tmp_path):
+    """tests/c/abi_from_c.c, built with gcc as C99 against include/pkv.h and
+    linked to libpkv.so, checks the ABI version, validation statuses and
+    messages, and the workspace-size queries, all on the host."""
+    exe = str(tmp_path / "abi_from_c")
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                        f"-I{os.path.dirname(HEADER)}", os.path.join(ROOT, "tests", "c",
+                                                                      "abi_from_c.c"),
+                        "-o", exe, f"-L{libdir}", "-l:libpkv.so", f"-Wl,-rpath,{libdir}"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
